@@ -1,0 +1,147 @@
+/*
+ * moe_ragged_bf16.h - C ABI of the deterministic ragged BF16 grouped GEMM for
+ * Mixture-of-Experts expert projections, built for AMD MI355X (gfx950).
+ *
+ * Operations (Cake ragged BF16 grouped GEMM API page, docs.flashinfer.ai,
+ * introduction and operations table), for every expert e with rows
+ * s_e = offs[e-1] (0 for e == 0) up to t_e = offs[e]:
+ *
+ *   fwd    Y [s_e:t_e] = X[s_e:t_e] @ W[e]^T        Y  [M, N]    bf16
+ *   dgrad  dX[s_e:t_e] = G[s_e:t_e] @ W[e]          dX [M, K]    bf16
+ *   wgrad  dW[e]       = G[s_e:t_e]^T @ X[s_e:t_e]  dW [E, N, K] bf16 or fp32
+ *
+ * with all operands bf16, products summed in fp32 in one fixed order (no atomics),
+ * so every output is bitwise identical from run to run on one device with one
+ * build.  An expert with no rows gets an exactly-zero (+0.0) dW.  wgrad can
+ * instead accumulate into an fp32 dW (a Megatron-style main_grad):
+ * dW[e] = RN32(dW[e] + G_e^T X_e), one IEEE fp32 add of the finished product per
+ * element, bitwise equal to adding this library's own overwrite dW (flashinfer
+ * PR #8924, "Design and numerics").
+ *
+ * Common conventions of every entry point below:
+ *
+ *  - Pointers.  Every tensor pointer is a DEVICE pointer on the current HIP
+ *    device.  Tensors are dense and row-major: X [m_rows, k], W [E, n, k],
+ *    G and Y [m_rows, n], dX [m_rows, k], dW [E, n, k] (k is the unit-stride
+ *    dimension of X, W, dX and dW; n of G and Y).  Every tensor pointer must be
+ *    16-byte aligned, except offs, which needs 4-byte alignment.  Pointers to
+ *    tensors with a row dimension (X, G, Y, dX) may be NULL when m_rows == 0;
+ *    all others must be non-NULL.
+ *  - Groups.  offs holds num_groups int32 cumulative END offsets, on the device;
+ *    the host never reads it.  A caller holding m_indptr[E + 1] (leading zero)
+ *    passes m_indptr + 1.  Offsets must be non-decreasing and within
+ *    [0, m_rows]; the kernels clamp them, so bad offsets never access memory out
+ *    of bounds, but the results are then unspecified.  Rows at or past
+ *    offs[E-1] belong to no group: fwd and dgrad leave those output rows
+ *    untouched and wgrad ignores them.
+ *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 256 with n % 256 == 0,
+ *    k >= 64 with k % 64 == 0 (the constraints the API page states for the
+ *    stable forward entry, adopted for all three operations).
+ *  - Ownership.  The caller owns every buffer.  The library allocates and frees
+ *    no device memory, never synchronises the stream or the device, keeps no
+ *    pointer after returning and reads no device memory on the host.  Inputs and
+ *    outputs must stay alive until the stream has passed the enqueued work.
+ *  - Streams.  All work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *    stream), in order.  Calls are thread-safe; the only global state is a
+ *    per-device property cache filled once.
+ *  - Errors.  Every entry returns an mdg_status.  On a validation error nothing
+ *    is enqueued and no output is touched.  No exception or abort crosses the
+ *    ABI.  A failed kernel launch returns MDG_EHIP.
+ */
+#ifndef MOE_RAGGED_BF16_H
+#define MOE_RAGGED_BF16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MDG_ABI_VERSION 1
+
+typedef enum {
+  MDG_OK = 0,
+  MDG_EINVAL = 1,        /* null pointer, negative size, misaligned pointer, bad enum */
+  MDG_EUNSUPPORTED = 2,  /* shape outside the supported set, or device is not gfx950 */
+  MDG_EOVERLAP = 3,      /* an output shares a byte with an input, offs or the workspace */
+  MDG_EWORKSPACE = 4,    /* wgrad workspace missing or smaller than required */
+  MDG_EHIP = 5           /* the HIP runtime reported an error when enqueueing */
+} mdg_status;
+
+typedef enum { MDG_BF16 = 0, MDG_FP32 = 1 } mdg_dtype;
+
+/* Version of this ABI (MDG_ABI_VERSION of the header the library was built with). */
+int mdg_abi_version(void);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mdg_status_string(int status);
+
+/*
+ * fwd: Y[s_e:t_e] = X[s_e:t_e] @ W[e]^T  (API page, operations table, "fwd").
+ *   x  [m_rows, k] bf16, read.        w [num_groups, n, k] bf16, read.
+ *   offs [num_groups] int32, read.    y [m_rows, n] bf16, written (rows of groups only).
+ * m_rows == 0 enqueues nothing.  y must not overlap x, w or offs.
+ */
+int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y,
+                         int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                         void* stream);
+
+/*
+ * dgrad: dX[s_e:t_e] = G[s_e:t_e] @ W[e], W read in place (API page, operations
+ * table, "dgrad").
+ *   g  [m_rows, n] bf16, read.        w [num_groups, n, k] bf16, read.
+ *   offs [num_groups] int32, read.    dx [m_rows, k] bf16, written (rows of groups only).
+ * m_rows == 0 enqueues nothing.  dx must not overlap g, w or offs.
+ */
+int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
+                           int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                           void* stream);
+
+/*
+ * Bytes of device workspace grouped_det_gemm_wgrad needs for these sizes: a small
+ * work table plus fp32 partial tiles of the fixed-order row split.  It depends
+ * on the sizes only (never on offs or the device), so the host can allocate it
+ * without a sync.  Returns 0 for invalid sizes.
+ */
+size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                              int32_t num_groups);
+
+/*
+ * wgrad: dW[e] = G[s_e:t_e]^T @ X[s_e:t_e]  (API page, operations table, "wgrad";
+ * accumulate from flashinfer PR #8924, "Deterministic weight-gradient
+ * accumulation" and "Design and numerics").
+ *   g [m_rows, n] bf16, read.   x [m_rows, k] bf16, read.   offs [num_groups] int32, read.
+ *   dw [num_groups, n, k] of dw_dtype (MDG_BF16 or MDG_FP32):
+ *      accumulate == 0: written; an expert with no rows gets +0.0 everywhere.
+ *      accumulate != 0: dw_dtype must be MDG_FP32; read and written as
+ *        dw = RN32(dw + dW_e) (the add is done for empty experts too, so -0.0
+ *        becomes +0.0 as an add of the zero dW would make it).  m_rows == 0 then
+ *        enqueues nothing and leaves dw unchanged.
+ *   workspace: device buffer of at least grouped_det_gemm_wgrad_workspace_bytes()
+ *      bytes, 256-byte aligned, owned by the caller, contents on entry ignored;
+ *      must not overlap any other argument.  Two calls that share a workspace must
+ *      be ordered on one stream.
+ * The rows of each expert are split into fixed-size consecutive chunks whose
+ * size depends only on (m_rows, n, k, num_groups); chunk partials are summed in
+ * chunk order by a second kernel on the same stream.  dw must not overlap g, x,
+ * offs or the workspace.
+ */
+int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
+                           int dw_dtype, int accumulate,
+                           int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Rows per chunk of the wgrad row split for these sizes (a pure function of the
+ * sizes; exposed so tests can build cases with and without a split).
+ * Returns 0 for invalid sizes.
+ */
+int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
+                                          int32_t num_groups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_RAGGED_BF16_H */

@@ -1,0 +1,77 @@
+"""ctypes loader of the gfx950 HIP library (``libmoe_ragged_bf16.so``).
+
+Argument marshalling only.  The library is required: if it is missing or fails
+to load, every call raises; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+MDG_OK, MDG_EINVAL, MDG_EUNSUPPORTED, MDG_EOVERLAP, MDG_EWORKSPACE, MDG_EHIP = range(6)
+MDG_BF16, MDG_FP32 = 0, 1
+
+EXPORTED = (
+    "mdg_abi_version",
+    "mdg_status_string",
+    "grouped_det_gemm_fwd",
+    "grouped_det_gemm_dgrad",
+    "grouped_det_gemm_wgrad",
+    "grouped_det_gemm_wgrad_workspace_bytes",
+    "grouped_det_gemm_wgrad_chunk_rows",
+)
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MdgError(RuntimeError):
+    """A non-OK status returned by the C ABI."""
+
+    def __init__(self, entry: str, status: int, message: str):
+        super().__init__(f"{entry}: status {status}: {message}")
+        self.entry = entry
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return the library, with argument types declared."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise ImportError(
+                f"{path} is missing: build the HIP library first "
+                "(python -m moe_ragged_bf16_amd.build)")
+        lib = ctypes.CDLL(path)
+        i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+        lib.mdg_abi_version.restype = ctypes.c_int
+        lib.mdg_abi_version.argtypes = []
+        lib.mdg_status_string.restype = ctypes.c_char_p
+        lib.mdg_status_string.argtypes = [ctypes.c_int]
+        for name in ("grouped_det_gemm_fwd", "grouped_det_gemm_dgrad"):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+        lib.grouped_det_gemm_wgrad.restype = ctypes.c_int
+        lib.grouped_det_gemm_wgrad.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                               i64, i64, i64, i32, vp, sz, vp]
+        lib.grouped_det_gemm_wgrad_workspace_bytes.restype = sz
+        lib.grouped_det_gemm_wgrad_workspace_bytes.argtypes = [i64, i64, i64, i32]
+        lib.grouped_det_gemm_wgrad_chunk_rows.restype = i64
+        lib.grouped_det_gemm_wgrad_chunk_rows.argtypes = [i64, i64, i64, i32]
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().mdg_status_string(status).decode()
+
+
+def check(entry: str, status: int) -> None:
+    if status != MDG_OK:
+        raise MdgError(entry, status, status_string(status))

@@ -1,0 +1,253 @@
+// C ABI of the deterministic ragged BF16 grouped GEMM (include/moe_ragged_bf16.h).
+//
+// Host side only: argument validation (before anything is enqueued, as the
+// accumulate description of flashinfer PR #8924 requires of its checks), the
+// sizing rules of the wgrad row split, and the kernel launches.  The host never
+// reads offs, never allocates and never synchronises.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "grouped_gemm.h"
+#include "moe_ragged_bf16.h"
+
+namespace mdg {
+
+// ----------------------------------------------------------------- sizing rules
+// Rows per chunk of the wgrad row split.  A pure function of the sizes, so the
+// chunking (and with it every bit of dW) never depends on the device, timing or
+// the workspace handed in.  It aims at >= kSplitTargetUnits work units even when
+// one expert holds all rows, and never splits below kMinChunkRows rows.
+constexpr int64_t kSplitTargetUnits = 512;
+constexpr int64_t kMinChunkRows = 256;
+
+int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  (void)num_groups;
+  const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
+  const int64_t want_chunks = (kSplitTargetUnits + tiles - 1) / tiles;
+  int64_t r = (m_rows + want_chunks - 1) / want_chunks;
+  r = (r + kTileR - 1) / kTileR * kTileR;
+  return r < kMinChunkRows ? kMinChunkRows : r;
+}
+
+// Upper bound on the number of experts with more than R rows.
+int64_t wgrad_max_split_groups(int64_t m_rows, int64_t chunk_rows, int32_t num_groups) {
+  const int64_t big = m_rows / (chunk_rows + 1);
+  return big < num_groups ? big : num_groups;
+}
+
+// Upper bound on sum over split experts of ceil(m_e / R):
+// sum ceil(m_e/R) <= sum floor(m_e/R) + #split <= floor(M/R) + #split.
+int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_groups) {
+  const int64_t big = wgrad_max_split_groups(m_rows, chunk_rows, num_groups);
+  return big == 0 ? 0 : m_rows / chunk_rows + big;
+}
+
+namespace {
+
+constexpr size_t kTableBytes = 4096;  // reserved head of the workspace
+
+struct DeviceInfo {
+  bool ok = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+
+DeviceInfo g_dev[64];
+std::once_flag g_dev_once[64];
+
+int query_device(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MDG_EHIP;
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    g_dev[dev].gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].ok = true;
+  });
+  if (!g_dev[dev].ok) return MDG_EHIP;
+  *out = g_dev[dev];
+  return MDG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return Range{lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+
+bool overlaps(Range a, Range b) {
+  if (a.hi == a.lo || b.hi == b.lo) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Shared size checks.  Sizes are kept small enough for the kernels' 32-bit
+// in-tile arithmetic: rows < 2^31, n and k < 2^20, and per-expert n*k < 2^31.
+int check_sizes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (m_rows < 0 || n <= 0 || k <= 0 || num_groups <= 0) return MDG_EINVAL;
+  if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
+  if (n % kTileI != 0 || k % kTileR != 0) return MDG_EUNSUPPORTED;
+  if (m_rows > INT32_MAX / 2 || n > (1 << 20) || k > (1 << 20) || n * k > INT32_MAX)
+    return MDG_EUNSUPPORTED;
+  return MDG_OK;
+}
+
+int persistent_grid(int64_t units_upper_bound, int cus) {
+  int64_t g = cus > 0 ? cus : 256;
+  if (units_upper_bound < g) g = units_upper_bound;
+  if (g >= 8) g -= g % 8;
+  return g < 1 ? 1 : (int)g;
+}
+
+int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
+                 int64_t n, int64_t k, int32_t num_groups, void* stream) {
+  int st = check_sizes(m_rows, n, k, num_groups);
+  if (st != MDG_OK) return st;
+  // Row-indexed tensors may be NULL when there are no rows (never dereferenced).
+  if (!w || !offs || (m_rows > 0 && (!a || !out))) return MDG_EINVAL;
+  if (!aligned16(a) || !aligned16(w) || !aligned4(offs) || !aligned16(out)) return MDG_EINVAL;
+  const int64_t a_cols = (op == kFwd) ? k : n;
+  const int64_t o_cols = (op == kFwd) ? n : k;
+  const Range ra = range_of(a, m_rows * a_cols * 2);
+  const Range rw = range_of(w, (int64_t)num_groups * n * k * 2);
+  const Range ro = range_of(offs, (int64_t)num_groups * 4);
+  const Range ry = range_of(out, m_rows * o_cols * 2);
+  if (overlaps(ry, ra) || overlaps(ry, rw) || overlaps(ry, ro)) return MDG_EOVERLAP;
+  if (m_rows == 0) return MDG_OK;
+
+  DeviceInfo dev;
+  st = query_device(&dev);
+  if (st != MDG_OK) return st;
+  if (!dev.gfx950) return MDG_EUNSUPPORTED;
+
+  GemmParams p{};
+  p.a = static_cast<const uint16_t*>(a);
+  p.b = static_cast<const uint16_t*>(w);
+  p.offs = offs;
+  p.out = out;
+  p.m_rows = m_rows;
+  p.n = (int32_t)n;
+  p.k = (int32_t)k;
+  p.num_groups = num_groups;
+  const int64_t n_j = (op == kFwd) ? n / kTileJ : (k + kTileJ - 1) / kTileJ;
+  const int64_t row_tiles_ub = (m_rows + kTileI - 1) / kTileI + num_groups;
+  const int grid = persistent_grid(row_tiles_ub * n_j, dev.cus);
+  if (launch_gemm(op, p, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return MDG_EHIP;
+  return MDG_OK;
+}
+
+}  // namespace
+}  // namespace mdg
+
+using namespace mdg;
+
+extern "C" {
+
+int mdg_abi_version(void) { return MDG_ABI_VERSION; }
+
+const char* mdg_status_string(int s) {
+  switch (s) {
+    case MDG_OK: return "ok";
+    case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
+    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 256 == 0, k % 64 == 0, 1 <= groups <= 1024)";
+    case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
+    case MDG_EWORKSPACE: return "wgrad workspace missing or too small";
+    case MDG_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
+                         int64_t n, int64_t k, int32_t num_groups, void* stream) {
+  return fwd_or_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, stream);
+}
+
+int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
+                           int64_t n, int64_t k, int32_t num_groups, void* stream) {
+  return fwd_or_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, stream);
+}
+
+int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return wgrad_chunk_rows(m_rows, n, k, num_groups);
+}
+
+size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
+  const int64_t slots = wgrad_max_partial_slots(m_rows, r, num_groups);
+  return kTableBytes + (size_t)slots * (size_t)n * (size_t)k * sizeof(float);
+}
+
+int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
+                           int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_sizes(m_rows, n, k, num_groups);
+  if (st != MDG_OK) return st;
+  if (dw_dtype != MDG_BF16 && dw_dtype != MDG_FP32) return MDG_EINVAL;
+  if (accumulate != 0 && dw_dtype != MDG_FP32) return MDG_EUNSUPPORTED;
+  if (!offs || !dw || (m_rows > 0 && (!g || !x))) return MDG_EINVAL;
+  if (!aligned16(g) || !aligned16(x) || !aligned4(offs) || !aligned16(dw)) return MDG_EINVAL;
+  const size_t need = grouped_det_gemm_wgrad_workspace_bytes(m_rows, n, k, num_groups);
+  if (!workspace || workspace_bytes < need) return MDG_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MDG_EINVAL;
+  const int64_t esz = dw_dtype == MDG_FP32 ? 4 : 2;
+  const Range rg = range_of(g, m_rows * n * 2);
+  const Range rx = range_of(x, m_rows * k * 2);
+  const Range ro = range_of(offs, (int64_t)num_groups * 4);
+  const Range rd = range_of(dw, (int64_t)num_groups * n * k * esz);
+  const Range rws = range_of(workspace, (int64_t)need);
+  if (overlaps(rd, rg) || overlaps(rd, rx) || overlaps(rd, ro) || overlaps(rd, rws)) return MDG_EOVERLAP;
+  if (overlaps(rws, rg) || overlaps(rws, rx) || overlaps(rws, ro)) return MDG_EOVERLAP;
+  // An accumulate over zero rows launches nothing and leaves dw unchanged.
+  if (m_rows == 0 && accumulate) return MDG_OK;
+
+  DeviceInfo dev;
+  st = query_device(&dev);
+  if (st != MDG_OK) return st;
+  if (!dev.gfx950) return MDG_EUNSUPPORTED;
+
+  const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
+  GemmParams p{};
+  p.a = static_cast<const uint16_t*>(g);
+  p.b = static_cast<const uint16_t*>(x);
+  p.offs = offs;
+  p.out = dw;
+  p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kTableBytes);
+  p.m_rows = m_rows;
+  p.n = (int32_t)n;
+  p.k = (int32_t)k;
+  p.num_groups = num_groups;
+  p.chunk_rows = (int32_t)r;
+  p.out_fp32 = dw_dtype == MDG_FP32;
+  p.accumulate = accumulate != 0;
+
+  const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
+  const int64_t units_ub = tiles * (num_groups + m_rows / r);
+  if (units_ub > INT32_MAX) return MDG_EUNSUPPORTED;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_gemm(kWgrad, p, persistent_grid(units_ub, dev.cus), s) != hipSuccess) return MDG_EHIP;
+  const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
+  if (split_ub > 0) {
+    const int64_t nk4 = n * k / 4;
+    int64_t gx = (nk4 + kThreads * 4 - 1) / (kThreads * 4);
+    const int64_t cap = (4 * (int64_t)(dev.cus > 0 ? dev.cus : 256) + split_ub - 1) / split_ub;
+    if (gx > cap) gx = cap;
+    if (gx < 1) gx = 1;
+    if (split_ub > 65535) return MDG_EUNSUPPORTED;
+    if (launch_wgrad_reduce(p, (int)gx, (int)split_ub, s) != hipSuccess) return MDG_EHIP;
+  }
+  return MDG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,42 @@
+// Internal interface between the C ABI (capi.cpp) and the gfx950 kernels
+// (grouped_gemm_kernels.hip).  Not installed; the public interface is
+// include/moe_ragged_bf16.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mdg {
+
+// Tile geometry shared by host and device code.
+constexpr int kTileI = 256;      // output tile extent along the first output dim
+constexpr int kTileJ = 256;      // output tile extent along the unit-stride output dim
+constexpr int kTileR = 64;       // reduction step staged per LDS buffer
+constexpr int kThreads = 256;    // 4 waves of 64
+constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
+
+enum Op : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
+
+struct GemmParams {
+  const uint16_t* a;      // fwd: X, dgrad: G, wgrad: G
+  const uint16_t* b;      // fwd: W, dgrad: W, wgrad: X
+  const int32_t* offs;    // [E] cumulative end offsets (device)
+  void* out;              // fwd: Y, dgrad: dX, wgrad: dW
+  float* partial;         // wgrad: fp32 partial tiles of split groups
+  int64_t m_rows;
+  int32_t n, k, num_groups;
+  int32_t chunk_rows;     // wgrad rows per chunk
+  int32_t out_fp32;       // wgrad: dW is fp32
+  int32_t accumulate;     // wgrad: dW = RN32(dW + product)
+};
+
+// Launchers (grouped_gemm_kernels.hip).  Return the HIP status of the launch.
+hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream);
+hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
+
+// Host-side sizing helpers (capi.cpp).
+int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);
+int64_t wgrad_max_split_groups(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
+int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
+
+}  // namespace mdg

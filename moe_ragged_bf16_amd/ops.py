@@ -1,0 +1,169 @@
+"""Python entry points over the C ABI, for torch tensors on a ROCm device.
+
+Each function marshals pointers, sizes and the current HIP stream and calls the
+library; every step of the computation runs in the gfx950 kernels.  torch
+supplies device memory (outputs and the wgrad workspace) and the stream.
+
+Signatures follow the one-shot functions of the Cake ragged BF16 grouped GEMM
+API page and flashinfer PR #8924 ("Deterministic weight-gradient
+accumulation"): grouped_det_gemm_fwd(x, w, offs), grouped_det_gemm_dgrad(g, w,
+offs) and grouped_det_gemm_wgrad(g, x, offs, out=None, out_dtype=None,
+num_groups=None, *, accumulate=False).  ``offs`` is the int32 device tensor of
+cumulative end offsets ``[E]`` or the ``m_indptr [E + 1]`` form with a leading
+zero (told apart by its length).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _capi
+
+__all__ = ["grouped_det_gemm_fwd", "grouped_det_gemm_dgrad", "grouped_det_gemm_wgrad",
+           "wgrad_workspace_bytes", "wgrad_chunk_rows"]
+
+
+def _stream_handle(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D, got shape {tuple(t.shape)}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a ROCm device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _offs_ptr(offs: torch.Tensor, E: int) -> int:
+    """Pointer to the E cumulative end offsets (skips m_indptr's leading zero)."""
+    if offs.dtype != torch.int32 or offs.dim() != 1 or offs.device.type != "cuda":
+        raise TypeError("offs must be a 1-D int32 device tensor")
+    if not offs.is_contiguous():
+        raise ValueError("offs must be contiguous")
+    if offs.numel() == E:
+        return offs.data_ptr()
+    if offs.numel() == E + 1:
+        return offs.data_ptr() + 4
+    raise ValueError(f"offs has {offs.numel()} entries; expected E={E} (offs) or E+1 (m_indptr)")
+
+
+def _same_device(*ts):
+    d = ts[0].device
+    for t in ts[1:]:
+        if t.device != d:
+            raise ValueError("all tensors must be on the same device")
+
+
+def grouped_det_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y[s_e:t_e] = X[s_e:t_e] @ W[e]^T, bf16 [M, N].  Rows past offs[E-1] of a
+    freshly allocated Y are left uninitialised."""
+    _need(x, "x", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    M, K = x.shape
+    E, N, K2 = w.shape
+    if K2 != K:
+        raise ValueError(f"x has K={K} but w has K={K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError(f"out must have shape {(M, N)}")
+    _same_device(x, w, offs, out)
+    op = _offs_ptr(offs, E)
+    with torch.cuda.device(x.device):
+        st = _capi.load_library().grouped_det_gemm_fwd(
+            x.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E, _stream_handle(x))
+    _capi.check("grouped_det_gemm_fwd", st)
+    return out
+
+
+def grouped_det_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX[s_e:t_e] = G[s_e:t_e] @ W[e], bf16 [M, K]."""
+    _need(g, "g", torch.bfloat16, 2)
+    _need(w, "w", torch.bfloat16, 3)
+    M, N = g.shape
+    E, N2, K = w.shape
+    if N2 != N:
+        raise ValueError(f"g has N={N} but w has N={N2}")
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=g.device)
+    _need(out, "out", torch.bfloat16, 2)
+    if tuple(out.shape) != (M, K):
+        raise ValueError(f"out must have shape {(M, K)}")
+    _same_device(g, w, offs, out)
+    op = _offs_ptr(offs, E)
+    with torch.cuda.device(g.device):
+        st = _capi.load_library().grouped_det_gemm_dgrad(
+            g.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E, _stream_handle(g))
+    _capi.check("grouped_det_gemm_dgrad", st)
+    return out
+
+
+def wgrad_workspace_bytes(m_rows: int, n: int, k: int, num_groups: int) -> int:
+    return int(_capi.load_library().grouped_det_gemm_wgrad_workspace_bytes(m_rows, n, k, num_groups))
+
+
+def wgrad_chunk_rows(m_rows: int, n: int, k: int, num_groups: int) -> int:
+    return int(_capi.load_library().grouped_det_gemm_wgrad_chunk_rows(m_rows, n, k, num_groups))
+
+
+def grouped_det_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor,
+                           out: Optional[torch.Tensor] = None, out_dtype=None,
+                           num_groups: Optional[int] = None, *, accumulate: bool = False,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dW[e] = G[s_e:t_e]^T @ X[s_e:t_e], [E, N, K] in bf16 or fp32.
+
+    With ``accumulate=True`` the product is added into ``out`` (fp32):
+    out = RN32(out + dW).  E comes from ``out``, else ``num_groups``, else the
+    length of ``offs``.  ``workspace`` (uint8 device tensor) is allocated when
+    not given.
+    """
+    if not isinstance(accumulate, bool):
+        raise TypeError("accumulate must be a bool")
+    _need(g, "g", torch.bfloat16, 2)
+    _need(x, "x", torch.bfloat16, 2)
+    M, N = g.shape
+    M2, K = x.shape
+    if M2 != M:
+        raise ValueError(f"g has {M} rows but x has {M2}")
+    if out is not None:
+        E = out.shape[0]
+    elif num_groups is not None:
+        E = int(num_groups)
+    else:
+        E = offs.numel()
+    if out_dtype is not None and out is not None and out.dtype != out_dtype:
+        raise TypeError("out_dtype must be None or equal to out.dtype")
+    if out is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs out")
+        dt = torch.bfloat16 if out_dtype is None else out_dtype
+        if dt not in (torch.bfloat16, torch.float32):
+            raise TypeError("out_dtype must be torch.bfloat16 or torch.float32")
+        out = torch.empty((E, N, K), dtype=dt, device=g.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _need(out, "out", out.dtype, 3)
+    if tuple(out.shape) != (E, N, K):
+        raise ValueError(f"out must have shape {(E, N, K)}")
+    _same_device(g, x, offs, out)
+    op = _offs_ptr(offs, E)
+    need = wgrad_workspace_bytes(M, N, K, E)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=g.device)
+    dt_code = _capi.MDG_FP32 if out.dtype == torch.float32 else _capi.MDG_BF16
+    with torch.cuda.device(g.device):
+        st = _capi.load_library().grouped_det_gemm_wgrad(
+            g.data_ptr(), x.data_ptr(), op, out.data_ptr(), dt_code, int(accumulate),
+            M, N, K, E, workspace.data_ptr(), workspace.numel(), _stream_handle(g))
+    _capi.check("grouped_det_gemm_wgrad", st)
+    return out

@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every declared symbol, and refuses bad
+arguments before touching the device (no GPU needed).
+
+Pointers below are fake, aligned addresses: every case returns before any
+device access, which is what the header promises for validation errors.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import moe_ragged_bf16_amd as mdg
+from moe_ragged_bf16_amd import _capi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ragged_bf16.h")
+
+OK, EINVAL, EUNSUP, EOVERLAP, EWS, EHIP = range(6)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mdg.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) == set(_capi.EXPORTED), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.mdg_abi_version() == 1
+    for s in range(6):
+        assert mdg.status_string(s)
+    assert mdg.status_string(99) == "unknown status"
+
+
+A, B, C, D, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+@pytest.mark.parametrize("fn", ["grouped_det_gemm_fwd", "grouped_det_gemm_dgrad"])
+def test_fwd_dgrad_refusals(lib, fn):
+    f = getattr(lib, fn)
+    # sizes
+    assert f(A, B, C, D, -1, 256, 256, 4, None) == EINVAL
+    assert f(A, B, C, D, 8, 0, 256, 4, None) == EINVAL
+    assert f(A, B, C, D, 8, 256, 256, 0, None) == EINVAL
+    assert f(A, B, C, D, 8, 128, 256, 4, None) == EUNSUP       # n % 256
+    assert f(A, B, C, D, 8, 256, 96, 4, None) == EUNSUP        # k % 64
+    assert f(A, B, C, D, 8, 256, 256, 1025, None) == EUNSUP    # too many groups
+    # pointers
+    assert f(0, B, C, D, 8, 256, 256, 4, None) == EINVAL
+    assert f(A, 0, C, D, 8, 256, 256, 4, None) == EINVAL
+    assert f(A, B, 0, D, 8, 256, 256, 4, None) == EINVAL
+    assert f(A, B, C, 0, 8, 256, 256, 4, None) == EINVAL
+    assert f(A + 8, B, C, D, 8, 256, 256, 4, None) == EINVAL   # 16-byte alignment
+    assert f(A, B, C + 2, D, 8, 256, 256, 4, None) == EINVAL   # offs needs 4 bytes
+    # overlap of the output with each input
+    assert f(A, B, C, A + 16, 8, 256, 256, 4, None) == EOVERLAP
+    assert f(A, B, C, B + 4096, 8, 256, 256, 4, None) == EOVERLAP
+    assert f(A, B, C, C - 16, 8, 256, 256, 4, None) == EOVERLAP
+    # zero rows: nothing to do, nothing enqueued; row tensors may then be NULL
+    assert f(A, B, C, D, 0, 256, 256, 4, None) == OK
+    assert f(0, B, C, 0, 0, 256, 256, 4, None) == OK
+    assert f(A, B, 0, D, 0, 256, 256, 4, None) == EINVAL      # offs is always needed
+
+
+def test_offs_plus_one_is_accepted_alignment(lib):
+    # the m_indptr form passes m_indptr + 1: 4-byte aligned only
+    assert lib.grouped_det_gemm_fwd(A, B, C + 4, D, 0, 256, 256, 4, None) == OK
+
+
+def test_wgrad_refusals(lib):
+    f = lib.grouped_det_gemm_wgrad
+    need = lib.grouped_det_gemm_wgrad_workspace_bytes(512, 256, 256, 4)
+    assert need > 0
+    args = dict(dt=1, acc=0, M=512, N=256, K=256, E=4, ws=WS, wsb=need)
+
+    def call(g=A, x=B, o=C, d=D, **kw):
+        a = dict(args)
+        a.update(kw)
+        return f(g, x, o, d, a["dt"], a["acc"], a["M"], a["N"], a["K"], a["E"], a["ws"], a["wsb"], None)
+
+    assert call(dt=2) == EINVAL                        # bad dtype code
+    assert call(dt=0, acc=1) == EUNSUP                 # bf16 accumulate is not offered
+    assert call(ws=0) == EWS                           # no workspace
+    assert call(wsb=need - 1) == EWS                   # short workspace
+    assert call(ws=WS + 16) == EINVAL                  # workspace alignment
+    assert call(d=A + 64) == EOVERLAP                  # dW over g
+    assert call(d=B) == EOVERLAP                       # dW over x
+    assert call(d=C - 64) == EOVERLAP                  # dW over offs
+    assert call(ws=D + 256) == EOVERLAP                # workspace over dW
+    assert call(ws=A) == EOVERLAP                      # workspace over g
+    assert call(M=-1) == EINVAL
+    assert call(N=300) == EUNSUP
+    # accumulate over zero rows leaves dW unchanged: nothing enqueued
+    need0 = lib.grouped_det_gemm_wgrad_workspace_bytes(0, 256, 256, 4)
+    assert call(M=0, acc=1, wsb=need0) == OK
+    assert call(g=0, x=0, M=0, acc=1, wsb=need0) == OK
+    assert call(g=0, M=8) == EINVAL
+
+
+def test_chunk_rows_rule(lib):
+    for (M, N, K, E) in [(512, 256, 256, 4), (16384, 14336, 4096, 8), (32768, 1536, 2048, 64),
+                         (32768, 4096, 7168, 128), (65536, 2048, 7168, 256), (0, 256, 64, 1),
+                         (100000, 256, 64, 1)]:
+        r = lib.grouped_det_gemm_wgrad_chunk_rows(M, N, K, E)
+        assert r >= 256 and r % 64 == 0
+        assert r == lib.grouped_det_gemm_wgrad_chunk_rows(M, N, K, E)
+    # big tiles per expert: no split at all for the 8-expert Mixtral-like shape
+    assert lib.grouped_det_gemm_wgrad_chunk_rows(16384, 14336, 4096, 8) >= 16384
+    assert lib.grouped_det_gemm_wgrad_chunk_rows(8, 200, 64, 1) == 0      # invalid sizes
+
+
+@pytest.mark.parametrize("M,N,K,E", [(512, 256, 256, 4), (5000, 256, 64, 3), (65536, 2048, 7168, 256),
+                                     (32768, 1536, 2048, 64), (1000, 256, 128, 1)])
+def test_workspace_covers_every_grouping(lib, M, N, K, E):
+    """The workspace bound holds for any split of M rows into E groups."""
+    R = lib.grouped_det_gemm_wgrad_chunk_rows(M, N, K, E)
+    have = lib.grouped_det_gemm_wgrad_workspace_bytes(M, N, K, E) - 4096
+    rng = np.random.default_rng(M + E)
+    cases = [np.full(E, M // E) for _ in range(1)]
+    cases.append(np.array([M] + [0] * (E - 1)))
+    for _ in range(200):
+        p = rng.dirichlet(np.full(E, rng.choice([0.05, 0.3, 1.0, 5.0])))
+        cases.append(rng.multinomial(M, p))
+    if E > 1:
+        cases.append(np.array([R + 1] * min(E, M // (R + 1)) + [0] * (E - min(E, M // (R + 1)))))
+    for s in cases:
+        slots = sum(-(-int(m) // R) for m in s if m > R)
+        assert slots * N * K * 4 <= have, (s, R)

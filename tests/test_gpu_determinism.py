@@ -1,0 +1,106 @@
+"""Bitwise contracts on the GPU: reruns, the fused accumulate and zero rows."""
+import numpy as np
+import pytest
+import torch
+
+import moe_ragged_bf16_amd as mdg
+from workloads import make_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _poison(t):
+    if t.dtype == torch.bfloat16:
+        t.view(torch.int16).random_(-32768, 32767)
+    else:
+        t.view(torch.int32).random_(-2**31, 2**31 - 1)
+
+
+@pytest.mark.parametrize("case", [dict(name="tiny"), dict(sizes=[0, 1000, 3000, 5, 0], N=256, K=320)])
+def test_reruns_bitwise_with_poisoned_outputs(case):
+    d = make_inputs(seed=5, device=DEV, **({"name": case["name"]} if "name" in case else
+                                            {"sizes": case["sizes"], "N": case["N"], "K": case["K"]}))
+    M, N, K, E = d["M"], d["N"], d["K"], d["E"]
+    first = None
+    for it in range(10):
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+        dw32 = torch.empty((E, N, K), dtype=torch.float32, device=DEV)
+        dw16 = torch.empty((E, N, K), dtype=torch.bfloat16, device=DEV)
+        for t in (y, dx, dw32, dw16):
+            _poison(t)
+        mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"], out=y)
+        mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"], out=dx)
+        mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=dw32)
+        mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=dw16)
+        cur = [y.view(torch.int16).clone(), dx.view(torch.int16).clone(),
+               dw32.view(torch.int32).clone(), dw16.view(torch.int16).clone()]
+        if first is None:
+            first = cur
+        else:
+            for a, b in zip(first, cur):
+                assert torch.equal(a, b), it
+
+
+def test_accumulate_equals_adding_own_dw():
+    d = make_inputs(sizes=[0, 1000, 3000, 5, 0, 77], N=512, K=320, seed=9, device=DEV,
+                    tensors=("x", "g", "main_grad"))
+    mg0 = d["main_grad"]
+    # plant -0.0 on an empty expert and on a used one
+    mg0[0, :3, :5] = -0.0
+    mg0[1, 7, 9] = -0.0
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    expect = mg0 + dw                      # AccumulateGrad of the det dW: one fp32 add
+    outs = []
+    for _ in range(3):
+        mg = mg0.clone()
+        mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=mg, accumulate=True)
+        outs.append(mg)
+    for mg in outs:
+        assert torch.equal(mg.view(torch.int32), expect.view(torch.int32))
+    assert not torch.signbit(outs[0][0, :3, :5]).any()      # -0.0 + 0.0 = +0.0
+
+
+def test_accumulate_zero_rows_leaves_out_unchanged():
+    E, N, K = 3, 256, 64
+    g = torch.empty((0, N), dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    offs = torch.zeros(E, dtype=torch.int32, device=DEV)
+    mg = torch.randn((E, N, K), device=DEV)
+    mg[0, 0, 0] = -0.0
+    before = mg.clone()
+    mdg.grouped_det_gemm_wgrad(g, x, offs, out=mg, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(mg.view(torch.int32), before.view(torch.int32))
+    # overwrite with zero rows writes +0.0
+    dw = mdg.grouped_det_gemm_wgrad(g, x, offs, out_dtype=torch.float32)
+    assert torch.all(dw.view(torch.int32) == 0)
+    y = mdg.grouped_det_gemm_fwd(x, torch.zeros((E, N, K), dtype=torch.bfloat16, device=DEV), offs)
+    assert y.shape == (0, N)
+
+
+def test_offsets_rewritten_in_place_give_new_result():
+    d = make_inputs(sizes=[100, 200, 300], N=256, K=128, seed=2, device=DEV)
+    y1 = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"]).clone()
+    d["offs"].copy_(torch.tensor([300, 300, 600], dtype=torch.int32, device=DEV))
+    y2 = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    ref2 = (d["x"][:300].float() @ d["w"][0].float().T)
+    torch.cuda.synchronize()
+    assert not torch.equal(y1[100:300], y2[100:300])
+    err = (y2[:300].float() - ref2).abs().max() / ref2.abs().max()
+    assert err < 2e-2
+
+
+def test_two_streams_same_bits():
+    d = make_inputs(sizes=[500, 0, 900], N=512, K=256, seed=4, device=DEV)
+    ref = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(s1):
+        a = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    with torch.cuda.stream(s2):
+        b = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(b.view(torch.int32), ref.view(torch.int32))

@@ -1,0 +1,150 @@
+"""GPU parity: the HIP path against the CPU oracle (fp64), element by element
+on small ragged cases and on sampled outputs at the full workload sizes."""
+import numpy as np
+import pytest
+import torch
+
+import moe_ragged_bf16_amd as mdg
+import oracle
+from workloads import make_inputs
+from _parity import TOL_BF16, TOL_FP32, bits, block_err, group_errs, values, ranges
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SENTINEL = 0x7FC1   # a NaN pattern: rows outside every group must keep it
+
+
+def _poisoned(shape, dtype):
+    if dtype == torch.bfloat16:
+        return torch.full(shape, SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    return torch.full(shape, float("nan"), dtype=torch.float32, device=DEV)
+
+
+def _run_all(d, wgrad_dtypes=(torch.bfloat16, torch.float32)):
+    M, N, K, E = d["M"], d["N"], d["K"], d["E"]
+    y = _poisoned((M, N), torch.bfloat16)
+    dx = _poisoned((M, K), torch.bfloat16)
+    mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"], out=y)
+    mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"], out=dx)
+    dws = {}
+    for dt in wgrad_dtypes:
+        dws[dt] = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=_poisoned((E, N, K), dt))
+    torch.cuda.synchronize()
+    return y, dx, dws
+
+
+def _check_full(d, label):
+    """Every output element against the fp64 oracle."""
+    y, dx, dws = _run_all(d)
+    X, W, G = bits(d["x"]), bits(d["w"]), bits(d["g"])
+    offs = d["offs"].cpu().numpy()
+    sizes = d["sizes"]
+    Mg = int(sizes.sum())
+    ry = oracle.fwd(X, W, offs)
+    rdx = oracle.dgrad(G, W, offs)
+    rdw = oracle.wgrad(G, X, offs)
+    ey = group_errs(values(y)[:Mg], ry[:Mg], sizes)
+    edx = group_errs(values(dx)[:Mg], rdx[:Mg], sizes)
+    assert max(ey, default=0) <= TOL_BF16, (label, "fwd", ey)
+    assert max(edx, default=0) <= TOL_BF16, (label, "dgrad", edx)
+    # rows past offs[E-1] are untouched
+    if Mg < d["M"]:
+        assert np.all(bits(y)[Mg:] == SENTINEL) and np.all(bits(dx)[Mg:] == SENTINEL), label
+    for dt, tol in ((torch.bfloat16, TOL_BF16), (torch.float32, TOL_FP32)):
+        dw = values(dws[dt])
+        errs = [block_err(dw[e], rdw[e]) for e in range(d["E"])]
+        assert max(errs) <= tol, (label, "wgrad", dt, errs)
+        for e, m in enumerate(sizes):
+            if m == 0:
+                raw = dws[dt].cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32)
+                assert torch.all(raw[e] == 0), (label, "empty expert must be +0.0", e)
+    # bf16 dW is the RNE rounding of the fp32 dW (one shared reduction)
+    assert torch.equal(dws[torch.float32].to(torch.bfloat16).view(torch.int16),
+                       dws[torch.bfloat16].view(torch.int16)), label
+
+
+def test_tiny_full():
+    d = make_inputs("tiny", seed=0, device=DEV)
+    _check_full(d, "tiny")
+
+
+def test_tiny_indptr_form():
+    d = make_inputs("tiny", seed=0, device=DEV)
+    y1 = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    y2 = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["m_indptr"])
+    dx1 = mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"])
+    dx2 = mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["m_indptr"])
+    w1 = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    w2 = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["m_indptr"], out_dtype=torch.float32, num_groups=4)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(dx1.view(torch.int16), dx2.view(torch.int16))
+    assert torch.equal(w1.view(torch.int32), w2.view(torch.int32))
+
+
+@pytest.mark.parametrize("sizes,N,K,pad", [
+    ([1], 256, 64, 0),                       # one row, one reduction step
+    ([0, 257, 0, 255, 256], 512, 320, 0),    # empties, tile +-1, k not a multiple of 256
+    ([300, 1, 2, 63, 64, 65], 256, 192, 5),  # row padding past the last group
+    ([0, 0, 0], 256, 128, 7),                # every group empty
+    ([1000, 3000], 256, 256, 0),             # long groups: wgrad row split
+    ([700], 768, 576, 0),                    # one group, several tiles in N and K
+])
+def test_small_ragged_full(sizes, N, K, pad):
+    d = make_inputs(sizes=sizes, N=N, K=K, extra_rows=pad, seed=3, device=DEV)
+    _check_full(d, f"sizes={sizes} N={N} K={K} pad={pad}")
+
+
+def test_wgrad_split_is_exercised():
+    # the cases above cover both a split (long groups) and no split
+    assert mdg.wgrad_chunk_rows(4000, 256, 256, 2) < 3000
+    assert mdg.wgrad_chunk_rows(512, 256, 256, 4) < 311
+
+
+# ---------------------------------------------------------------- full sizes
+def _sample_rows(sizes, per_group, rng):
+    rows = []
+    for s, t in ranges(sizes):
+        if t == s:
+            continue
+        pick = {s, t - 1, min(t - 1, s + 255), min(t - 1, s + 256)}
+        pick |= set(rng.integers(s, t, per_group).tolist())
+        rows.extend(sorted(pick))
+    return np.array(rows, dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["mixtral", "fine"])
+def test_full_size_sampled(name):
+    d = make_inputs(name, seed=0, device=DEV)
+    rng = np.random.default_rng(1)
+    y = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    dx = mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"])
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    sizes = d["sizes"]
+    offs = d["offs"].cpu().numpy()
+    rows = _sample_rows(sizes, 6, rng)
+    rows_t = torch.from_numpy(rows).to(DEV)
+    X = bits(d["x"][rows_t])
+    G = bits(d["g"][rows_t])
+    W = bits(d["w"])
+    # sampled rows keep their group: build a compact offs over the sample
+    owner = np.searchsorted(offs, rows, side="right")
+    sub_sizes = np.bincount(owner, minlength=d["E"])
+    sub_offs = np.cumsum(sub_sizes).astype(np.int32)
+    ry = oracle.fwd(X, W, sub_offs)
+    rdx = oracle.dgrad(G, W, sub_offs)
+    gy, gdx = values(y[rows_t]), values(dx[rows_t])
+    assert max(group_errs(gy, ry, sub_sizes)) <= TOL_BF16
+    assert max(group_errs(gdx, rdx, sub_sizes)) <= TOL_BF16
+    # wgrad: sampled dW rows (n) of every non-empty expert, plus empty experts
+    n_pick = np.unique(np.concatenate([[0, d["N"] - 1], rng.integers(0, d["N"], 6)]))
+    for e, (s, t) in enumerate(ranges(sizes)):
+        got = dw[e][torch.from_numpy(n_pick).to(DEV)]
+        if t == s:
+            assert torch.all(got.view(torch.int32) == 0)
+            continue
+        Ge = bits(d["g"][s:t][:, torch.from_numpy(n_pick).to(DEV)].contiguous())
+        Xe = bits(d["x"][s:t])
+        ref = oracle.wgrad_expert(Ge, Xe)
+        assert block_err(values(got), ref) <= TOL_FP32, (name, e)
