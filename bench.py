@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of the deterministic ragged BF16 grouped GEMM on one MI355X.
+
+One step = one pass of the whole hot path over one batch of the workload:
+fwd (Y = X W^T per group), dgrad (dX = G W per group) and wgrad with the fused
+fp32 accumulate into main_grad (dW = G^T X per expert, added into main_grad),
+i.e. the expert-projection GEMMs of one MoE layer's training step.
+
+Prints ONE JSON line.  `value` is the step's grouped-GEMM throughput in TFLOP/s
+(3 x 2*M*N*K algorithmic FLOPs per step over the measured step time), with all
+inputs resident in HBM.  `roofline` reports the dominant kernel against the
+MI355X dense bf16 MFMA peak; `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload (rank 0 only).
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload mixtral]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["tiny", "mixtral", "fine", "skewed", "stress"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(d, target_s: float):
+    """Time the CPU oracle (fp64, as it stands) on whole experts of the workload,
+    in expert order, until about target_s seconds have been spent."""
+    import numpy as np
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+
+    def bits(t):
+        import torch
+        return t.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+    sizes = d["sizes"]
+    N, K = d["N"], d["K"]
+    flops = 0.0
+    spent = 0.0
+    used = []
+    s = 0
+    for e, m in enumerate(sizes):
+        m = int(m)
+        t0, t1 = s, s + m
+        s = t1
+        if m == 0:
+            continue
+        X = bits(d["x"][t0:t1])
+        G = bits(d["g"][t0:t1])
+        W = bits(d["w"][e:e + 1])
+        offs = np.array([m], dtype=np.int32)
+        c0 = time.perf_counter()
+        oracle.fwd(X, W, offs)
+        oracle.dgrad(G, W, offs)
+        oracle.wgrad(G, X, offs)
+        spent += time.perf_counter() - c0
+        flops += 3 * 2.0 * m * N * K
+        used.append((e, m))
+        if spent >= target_s:
+            break
+    rows = sum(m for _, m in used)
+    return {
+        "value": flops / spent / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"experts {used[0][0]}..{used[-1][0]} ({len(used)} experts, {rows} rows) of the "
+                   f"workload, fwd+dgrad+wgrad in fp64 NumPy, {spent:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_ragged_bf16_amd as mdg
+    from workloads import CONFIGS, make_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = CONFIGS[args.workload]
+    d = make_inputs(args.workload, seed=0, device=dev, tensors=("x", "w", "g", "main_grad"))
+    M, N, K, E = d["M"], d["N"], d["K"], d["E"]
+    x, w, g, offs, mg = d["x"], d["w"], d["g"], d["offs"], d["main_grad"]
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(mdg.wgrad_workspace_bytes(M, N, K, E), 256), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mdg.grouped_det_gemm_fwd(x, w, offs, out=y)
+        if ev is not None:
+            ev[1].record()
+        mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx)
+        if ev is not None:
+            ev[2].record()
+        mdg.grouped_det_gemm_wgrad(g, x, offs, out=mg, accumulate=True, workspace=ws)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(events[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    op_ms = {
+        "fwd": float(np.mean([e[0].elapsed_time(e[1]) for e in events])),
+        "dgrad": float(np.mean([e[1].elapsed_time(e[2]) for e in events])),
+        "wgrad_fp32_accumulate": float(np.mean([e[2].elapsed_time(e[3]) for e in events])),
+    }
+    flop_op = 2.0 * M * N * K
+    value = 3 * flop_op / (ms_per_step * 1e-3) / 1e12
+
+    # bitwise rerun check of the measured kernels (outputs must not change)
+    y_ref = y.clone()
+    dx_ref = dx.clone()
+    mdg.grouped_det_gemm_fwd(x, w, offs, out=y)
+    mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx)
+    torch.cuda.synchronize()
+    rerun_ok = bool(torch.equal(y.view(torch.int16), y_ref.view(torch.int16)) and
+                    torch.equal(dx.view(torch.int16), dx_ref.view(torch.int16)))
+    if not rerun_ok:
+        print("bitwise rerun check FAILED", file=sys.stderr)
+        sys.exit(1)
+
+    sizes = d["sizes"]
+    e_ne = int((sizes > 0).sum())
+    ops = {}
+    for name, ms in op_ms.items():
+        tf = flop_op / (ms * 1e-3) / 1e12
+        ops[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "pct_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 1)}
+    # dominant kernel: the op with the largest average launch time
+    dom = max(op_ms, key=op_ms.get)
+    achieved = flop_op / (op_ms[dom] * 1e-3) / 1e12
+    traffic = None
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "kernel": dom,
+                "flops_per_launch": flop_op}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(d, args.cpu_seconds)
+
+    line = {
+        "metric": "grouped GEMM TFLOP/s (fwd/dgrad/wgrad) + % of bf16 MFMA peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded routing and N(0,1) operands, bf16)",
+        "config": {"workload": cfg.name, "description": cfg.description, "E": E, "K": K, "N": N,
+                   "sum_m": M, "nonempty_experts": e_ne,
+                   "step": "fwd + dgrad + wgrad(fp32, fused accumulate into main_grad)"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 1),
+        "ops": ops,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rerun_bitwise": rerun_ok,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

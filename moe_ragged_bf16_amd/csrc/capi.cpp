@@ -29,7 +29,7 @@ int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_group
   const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
   const int64_t want_chunks = (kSplitTargetUnits + tiles - 1) / tiles;
   int64_t r = (m_rows + want_chunks - 1) / want_chunks;
-  r = (r + kTileR - 1) / kTileR * kTileR;
+  r = (r + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
   return r < kMinChunkRows ? kMinChunkRows : r;
 }
 
@@ -96,7 +96,7 @@ bool overlaps(Range a, Range b) {
 int check_sizes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (m_rows < 0 || n <= 0 || k <= 0 || num_groups <= 0) return MDG_EINVAL;
   if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
-  if (n % kTileI != 0 || k % kTileR != 0) return MDG_EUNSUPPORTED;
+  if (n % kTileI != 0 || k % kKAlign != 0) return MDG_EUNSUPPORTED;
   if (m_rows > INT32_MAX / 2 || n > (1 << 20) || k > (1 << 20) || n * k > INT32_MAX)
     return MDG_EUNSUPPORTED;
   return MDG_OK;

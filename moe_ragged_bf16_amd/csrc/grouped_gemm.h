@@ -11,7 +11,10 @@ namespace mdg {
 // Tile geometry shared by host and device code.
 constexpr int kTileI = 256;      // output tile extent along the first output dim
 constexpr int kTileJ = 256;      // output tile extent along the unit-stride output dim
-constexpr int kTileR = 64;       // reduction step staged per LDS buffer
+constexpr int kTileR = 32;       // reduction depth of one LDS stage
+constexpr int kStages = 4;       // LDS stages (kStages - 1 in flight)
+constexpr int kKAlign = 64;      // k must be a multiple of this (the ABI's contract)
+constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
 

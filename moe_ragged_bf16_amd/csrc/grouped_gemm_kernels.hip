@@ -5,31 +5,37 @@
 //   fwd    Y [s_e:t_e] = X[s_e:t_e] @ W[e]^T
 //   dgrad  dX[s_e:t_e] = G[s_e:t_e] @ W[e]          (W read in place)
 //   wgrad  dW[e]       = G[s_e:t_e]^T @ X[s_e:t_e]
-// All three are written as one tile GEMM  C[i][j] = sum_r A(i, r) * B(j, r):
-//   fwd    i = row, j = n, r = k:  A = X (r contiguous),  B = W[e]   (r contiguous)
-//   dgrad  i = row, j = k, r = n:  A = G (r contiguous),  B = W[e]   (j contiguous)
-//   wgrad  i = n,   j = k, r = row: A = G (i contiguous), B = X      (j contiguous)
+// All three are one tile GEMM  C[i][j] = sum_r A(i, r) * B(j, r):
+//   fwd    i = row, j = n, r = k:   A = X (r contiguous),   B = W[e] (r contiguous)
+//   dgrad  i = row, j = k, r = n:   A = G (r contiguous),   B = W[e] (j contiguous)
+//   wgrad  i = n,   j = k, r = row: A = G (i contiguous),   B = X    (j contiguous)
 //
 // Structure of one launch:
 //  * Offsets are read on the device only.  Each workgroup loads offs into LDS,
 //    clamps them to a non-decreasing sequence in [0, M] (bad offsets stay memory
-//    safe) and builds, with block-wide scans, the prefix of work units per
-//    group.  No host sync, no atomics.
-//  * Persistent grid: workgroup b walks units t = v(b), v(b) + P, ... where v
-//    spreads consecutive workgroup ids (which the hardware deals round-robin
-//    over the 8 XCDs) so that each XCD works on a contiguous run of units and
-//    the tiles it runs at once share operand panels in its L2.
+//    safe and groups never overlap) and builds, with block-wide scans, the
+//    prefix of work units per group.  No host sync, no atomics.
+//  * Persistent grid: workgroup b walks units v(b), v(b) + P, ... where v
+//    spreads consecutive workgroup ids (dealt round-robin over the 8 XCDs) so
+//    that each XCD works on a contiguous run of units, whose tiles share operand
+//    panels in that XCD's L2.
 //  * Units are 256 x 256 output tiles (fwd/dgrad: one row tile of one group;
-//    wgrad: one row chunk of one expert).  The reduction is staged 64 at a time
-//    through double-buffered LDS (one barrier per step), read back with 16-byte
-//    ds_read into v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the
-//    reduction order is fixed, so results are bitwise reproducible.
-//  * Operands whose reduction index is strided in memory (W in dgrad, G and X in
-//    wgrad) are loaded as 8 x 8 blocks and transposed in registers before the
-//    LDS store, so LDS always holds reduction-contiguous rows.
-//  * Rows past a group's end (or past a chunk's end) load as zero and are never
-//    stored.  wgrad row chunks of a split expert write fp32 partials that a
-//    second kernel adds in chunk order (fixed-order split of the reduction).
+//    wgrad: one row chunk of one expert).  The reduction is staged 64 deep into
+//    double-buffered LDS by buffer loads that write LDS directly (no registers);
+//    the buffer range check turns rows past a group's or chunk's end into zeros.
+//    The next stage's loads are in flight while the MFMAs of the current stage
+//    run; the next unit's first stage loads during the current epilogue.
+//  * LDS layouts follow the memory layout of each operand, with a 16-byte-chunk
+//    XOR swizzle so that both the DMA writes and the fragment reads are free of
+//    bank conflicts:
+//      r-contiguous operand  [256 rows][64 r]  read with ds_read_b128;
+//      i/j-contiguous operand [64 r][256 cols] read with ds_read_b64_tr_b16, the
+//      gfx950 transposing LDS read, which hands each lane 4 consecutive r of one
+//      column, so no operand is ever transposed in registers or in HBM.
+//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators, one fixed reduction order:
+//    results are bitwise reproducible.
+//  * wgrad row chunks of a split expert write fp32 partials that a second
+//    kernel adds in chunk order (a fixed-order split of the reduction).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -40,14 +46,18 @@ namespace mdg {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kLdsRow = kTileR + 8;  // bf16 elements per LDS row (144 bytes: conflict-free 16-byte reads)
-constexpr int kLdsTile = kTileI * kLdsRow;
-static_assert(kTileI == kTileJ, "square tiles assumed by the loaders");
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kStageBytes = kTileI * kTileR * 2;  // one operand, one stage: 16 KiB
+static_assert(kTileI == kTileJ, "square tiles assumed by the stage layout");
+static_assert(kStageBytes == 16 * 1024, "a stage is 16 segments of 1 KiB (one wave load each)");
+static_assert(kTileR == 32 && kStages == 4, "the pipeline below is written for 4 stages of 32");
 
 // ---------------------------------------------------------------------------
 // block-wide scans (256 threads = 4 waves of 64)
@@ -98,8 +108,10 @@ __device__ __forceinline__ int block_excl_max(int v, int* scratch) {
   return max(before, excl);
 }
 
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // ---------------------------------------------------------------------------
-// per-group work: the same rule in the GEMM kernel and the reduce kernel
+// per-group work: one rule for the GEMM kernel and the reduce kernel
 // ---------------------------------------------------------------------------
 struct UnitShape {
   int n_i, n_j;  // tiles along i and j of one slice
@@ -217,95 +229,182 @@ __device__ __forceinline__ void panel_order(int u, int rows, int cols, int gm, i
 }
 
 // ---------------------------------------------------------------------------
-// global -> register -> LDS staging
+// LDS stage layouts and the DMA that fills them
 // ---------------------------------------------------------------------------
-// Operand whose reduction index is contiguous: 256 rows x 64 reduction values.
-// Thread t loads rows 32q + t/8 (q = 0..7), 16 bytes at reduction offset 8*(t%8):
-// eight threads cover one 128-byte row segment.
-struct LoadRC {
-  u32x4 v[8];
+// "RC" operand (reduction contiguous in memory): 256 rows x 32 r, 64-byte LDS
+// rows; 16-byte chunk c of row `row` lives at chunk c ^ swz_rc(row).  Any 16
+// consecutive rows reading one logical chunk hit 16 distinct 16-byte bank
+// groups (and any 8 consecutive rows, 8 distinct ones in a 128-byte window).
+__device__ __forceinline__ int swz_rc(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// "TC" operand (tile columns contiguous in memory): 32 r x 256 columns,
+// 512-byte LDS rows; chunk c of row r lives at chunk c ^ swz_tc(r % 4) with the
+// table (0, 4, 10, 14): the 4 rows x 64 bytes read by 32 lanes of a transposing
+// read land on distinct bank groups.
+__device__ __forceinline__ int swz_tc(int r) {
+  const int k = r & 3;
+  return (k & 1) * 4 + (k & 2) * 5;
+}
 
-  __device__ __forceinline__ void load(const uint16_t* base, int ld, int rows_valid, int r0) {
-    const int t = threadIdx.x;
-    const int rr = t >> 3, pk = (t & 7) * 8;
+// Per-lane byte offsets (relative to the stage's first element in memory) of
+// this wave's 4 DMA loads of one operand stage.  The 16 KiB stage is 16 segments
+// of 1 KiB; wave w fills segments q*4 + w, q = 0..3; within a segment lane l
+// writes LDS bytes [16 l, 16 l + 16).
+template <bool TC>
+__device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int ld_bytes, int w, int lane) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int row = q * 32 + rr;
-      if (row < rows_valid)
-        v[q] = *reinterpret_cast<const u32x4*>(base + (size_t)row * ld + r0 + pk);
-      else
-        v[q] = u32x4{0u, 0u, 0u, 0u};
+  for (int q = 0; q < 4; ++q) {
+    const int seg = q * 4 + w;
+    if (!TC) {
+      const int row = seg * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ swz_rc(row);
+      off[q] = (uint32_t)(row * ld_bytes + c * 16);
+    } else {
+      const int r = seg * 2 + (lane >> 5);
+      const int c = (lane & 31) ^ swz_tc(r);
+      off[q] = (uint32_t)(r * ld_bytes + c * 16);
     }
   }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    const int t = threadIdx.x;
-    const int rr = t >> 3, pk = (t & 7) * 8;
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      *reinterpret_cast<u32x4*>(s + (q * 32 + rr) * kLdsRow + pk) = v[q];
-  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
+  if (bytes < 0) bytes = 0;
+  if (bytes > 0x7FFFFFF0) bytes = 0x7FFFFFF0;
+  // word 3: 32-bit data format, raw (unswizzled) addressing
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Operand of one unit: where its data starts and how much of it is real.
+struct Operand {
+  const uint8_t* base;  // element (first row, first column) of the unit's panel
+  const uint8_t* end;   // one past the tensor's last byte (memory-safety clip)
+  int ld_bytes;         // row stride in memory
+  int rows_valid;       // RC: valid rows of the 256-row panel; TC: valid reduction rows
+  int red_len;          // RC: reduction extent (stages at or past it load zeros)
 };
 
-// Operand whose tile index is contiguous and reduction index strided:
-// 64 reduction rows x 256 tile columns in memory.  Thread t loads the 8 x 8
-// block of reduction rows 8*(t%8) .. +7 and tile columns 8*(t/8) .. +7 and
-// stores it transposed (8 tile rows of 8 reduction values).
-struct LoadTC {
-  u32x4 v[8];
+// Issues this wave's DMA loads of reduction stage `kt` of one operand.  The
+// buffer's range check zero-fills everything past the valid rows.
+template <bool TC>
+__device__ __forceinline__ void dma_stage(const Operand& o, const uint32_t (&off)[4], uint8_t* lds_stage,
+                                          int kt, int w) {
+  const int r0 = kt * kTileR;
+  const uint8_t* base;
+  int64_t bytes;
+  if (!TC) {
+    base = o.base + (int64_t)r0 * 2;
+    bytes = r0 < o.red_len ? (int64_t)o.rows_valid * o.ld_bytes - (int64_t)r0 * 2 : 0;
+  } else {
+    base = o.base + (int64_t)r0 * o.ld_bytes;
+    int rows = o.rows_valid - r0;
+    rows = rows < 0 ? 0 : (rows > kTileR ? kTileR : rows);
+    bytes = (int64_t)rows * o.ld_bytes;
+  }
+  const int64_t left = o.end - base;
+  if (bytes > left) bytes = left;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_stage + (q * 4 + w) * 1024), 16, off[q], 0, 0,
+                                             0);
+}
 
-  __device__ __forceinline__ void load(const uint16_t* base, int ld, int red_valid, int cols_valid, int r0) {
-    const int t = threadIdx.x;
-    const int pr = (t & 7) * 8, cb = (t >> 3) * 8;
-    const bool cv = cb < cols_valid;
-    const uint16_t* b = base + (size_t)r0 * ld + cb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = pr + j;
-      if (cv && r0 + r < red_valid)
-        v[j] = *reinterpret_cast<const u32x4*>(b + (size_t)r * ld);
-      else
-        v[j] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* s) const {
-    const int t = threadIdx.x;
-    const int pr = (t & 7) * 8, cb = (t >> 3) * 8;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      u32x4 w;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t lo = v[2 * d][q >> 1], hi = v[2 * d + 1][q >> 1];
-        w[d] = (q & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-      }
-      *reinterpret_cast<u32x4*>(s + (cb + q) * kLdsRow + pr) = w;
-    }
-  }
-};
+// Waits until at most `kVm` of this wave's vector memory operations are
+// outstanding and all its LDS reads have returned.
+template <int kVm>
+__device__ __forceinline__ void wait_vm_lgkm() {
+  static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier for the stage ring.  __syncthreads() would also make the
+// compiler drain every outstanding load (its workgroup fence waits for all
+// vector memory operations), which would serialise the LDS-DMA prefetch; the
+// stage waits are explicit instead (wait_vm_lgkm before each barrier), and the
+// empty asm statements keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// DMA loads per stage per wave (both operands).
+constexpr int kDmaPerStage = 8;
+
+// Waits for stage `next` when `ahead` later stages may still be in flight.
+__device__ __forceinline__ void wait_stage(int ahead) {
+  if (ahead >= 2) wait_vm_lgkm<2 * kDmaPerStage>();
+  else if (ahead == 1) wait_vm_lgkm<kDmaPerStage>();
+  else wait_vm_lgkm<0>();
+}
 
 // ---------------------------------------------------------------------------
-// MFMA over one staged 64-deep reduction step
+// MFMA fragments from LDS
 // ---------------------------------------------------------------------------
+// Fragment of a 32 x 16 block (32 tile rows starting at `row0`, reduction
+// 16*kk .. 16*kk+15 of the stage): lane l holds row row0 + l%32, reduction
+// 8*(l/32) .. +7.
+template <bool TC>
+__device__ __forceinline__ bf16x8 load_frag(const uint8_t* st, int row0, int kk, int lane) {
+  if (!TC) {
+    const int row = row0 + (lane & 31);
+    const int c = (kk * 2 + (lane >> 5)) ^ swz_rc(row);
+    return *reinterpret_cast<const bf16x8*>(st + row * 64 + c * 16);
+  } else {
+    // ds_read_b64_tr_b16: within each 16-lane group, lane s addresses
+    // T[r0 + s/4][m0 + 4 (s%4)] (4 columns) and receives T[r0 + q][m0 + s],
+    // q = 0..3.  Two reads give the 8 reductions of the fragment.
+    const int g = lane >> 4, s = lane & 15;
+    const int col = row0 + 16 * (g & 1) + 4 * (s & 3);
+    const int chunk = (col >> 3) ^ swz_tc(s >> 2);  // r % 4 == s / 4 for both reads
+    const int half = (s & 1) * 8;
+    const int r_lo = kk * 16 + 8 * (g >> 1) + (s >> 2);
+    const uint8_t* p0 = st + r_lo * 512 + chunk * 16 + half;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
+    const s16x4 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * 512));
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <bool ATC, bool BTC>
+__device__ __forceinline__ void load_frags(bf16x8 (&fa)[4], bf16x8 (&fb)[4], const uint8_t* sa, const uint8_t* sb,
+                                           int wi, int wj, int kk, int lane) {
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    fa[b] = load_frag<ATC>(sa, wi * 128 + b * 32, kk, lane);
+    fb[b] = load_frag<BTC>(sb, wj * 128 + b * 32, kk, lane);
+  }
+}
+
 // Wave w owns the 128 x 128 sub-tile (i: 128*(w/2), j: 128*(w%2)) as 4 x 4
 // blocks of 32 x 32.  The MFMA is issued as D = Bfrag x Afrag, so D's rows are
 // j: lane l then holds i = l%32 and four consecutive j per register quad.
-__device__ __forceinline__ void mma_step(f32x16 (&acc)[4][4], const uint16_t* sa, const uint16_t* sb,
-                                         int wi, int wj, int lane) {
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
+__device__ __forceinline__ void mma_16(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
 #pragma unroll
-  for (int kk = 0; kk < kTileR / 16; ++kk) {
-    bf16x8 fa[4], fb[4];
+  for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      fa[b] = *reinterpret_cast<const bf16x8*>(sa + (wi * 128 + b * 32 + lr) * kLdsRow + kk * 16 + lk);
-      fb[b] = *reinterpret_cast<const bf16x8*>(sb + (wj * 128 + b * 32 + lr) * kLdsRow + kk * 16 + lk);
-    }
+    for (int jb = 0; jb < 4; ++jb)
+      acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[jb], fa[ib], acc[ib][jb], 0, 0, 0);
+}
+
+// 16 MFMAs on (fa0, fb0) while the LDS reads into (fa1, fb1) of step `kk` are
+// interleaved between them (scheduling groups pin the order).
+template <bool ATC, bool BTC>
+__device__ __forceinline__ void mma_16_with_reads(f32x16 (&acc)[4][4], const bf16x8 (&fa0)[4],
+                                                  const bf16x8 (&fb0)[4], bf16x8 (&fa1)[4], bf16x8 (&fb1)[4],
+                                                  const uint8_t* sa, const uint8_t* sb, int wi, int wj, int kk,
+                                                  int lane) {
+  constexpr int kReads = 4 * (ATC ? 2 : 1) + 4 * (BTC ? 2 : 1);
+  constexpr int kPer = 16 / kReads;
+  load_frags<ATC, BTC>(fa1, fb1, sa, sb, wi, wj, kk, lane);
+  mma_16(acc, fa0, fb0);
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-        acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[jb], fa[ib], acc[ib][jb], 0, 0, 0);
+  for (int r = 0; r < kReads; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
   }
+  if (16 - kPer * kReads > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - kPer * kReads, 0);
 }
 
 // fp32 -> bf16 with round to nearest, ties to even (NaN stays NaN).
@@ -318,8 +417,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Epilogue store modes.
 enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2 };
 
-// Writes the accumulators of this wave's sub-tile to `out` (row stride ldc),
-// rows i < i_valid and columns j < j_valid of the 256 x 256 tile.
+// Writes this wave's accumulators to `out` (row stride ldc elements), rows
+// i < i_valid and columns j < j_valid of the 256 x 256 tile.
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out, int64_t ldc, int i_valid,
                                            int j_valid, int wi, int wj, int lane, int mode) {
   const int lr = lane & 31, lh = (lane >> 5) * 4;
@@ -327,44 +426,226 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out,
   for (int ib = 0; ib < 4; ++ib) {
     const int i = wi * 128 + ib * 32 + lr;
     if (i >= i_valid) continue;
+    if (mode == kStoreBf16) {
+      uint16_t* o = static_cast<uint16_t*>(out) + i * ldc;
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
+      for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int j = wj * 128 + jb * 32 + g * 8 + lh;
-        if (j >= j_valid) continue;
-        const f32x16& a = acc[ib][jb];
-        if (mode == kStoreBf16) {
-          uint16_t* o = static_cast<uint16_t*>(out) + i * ldc + j;
+        for (int g = 0; g < 4; ++g) {
+          const int j = wj * 128 + jb * 32 + g * 8 + lh;
+          if (j >= j_valid) continue;
+          const f32x16& a = acc[ib][jb];
           u32x2 pk;
           pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
           pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
-          *reinterpret_cast<u32x2*>(o) = pk;
-        } else if (mode == kStoreF32) {
-          float* o = static_cast<float*>(out) + i * ldc + j;
-          *reinterpret_cast<f32x4*>(o) = f32x4{a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-        } else {
-          float* o = static_cast<float*>(out) + i * ldc + j;
-          f32x4 old = *reinterpret_cast<const f32x4*>(o);
-          // One IEEE fp32 add per element of the finished product (no contraction).
-          old[0] = __fadd_rn(old[0], a[4 * g + 0]);
-          old[1] = __fadd_rn(old[1], a[4 * g + 1]);
-          old[2] = __fadd_rn(old[2], a[4 * g + 2]);
-          old[3] = __fadd_rn(old[3], a[4 * g + 3]);
-          *reinterpret_cast<f32x4*>(o) = old;
+          *reinterpret_cast<u32x2*>(o + j) = pk;
         }
-      }
+    } else if (mode == kStoreF32) {
+      float* o = static_cast<float*>(out) + i * ldc;
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = wj * 128 + jb * 32 + g * 8 + lh;
+          if (j >= j_valid) continue;
+          const f32x16& a = acc[ib][jb];
+          *reinterpret_cast<f32x4*>(o + j) = f32x4{a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        }
+    } else {
+      // Read-modify-write: all 16 reads of the row block are issued before the
+      // first add, so their latencies overlap.
+      float* o = static_cast<float*>(out) + i * ldc;
+      f32x4 old[4][4];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = wj * 128 + jb * 32 + g * 8 + lh;
+          if (j < j_valid) old[jb][g] = *reinterpret_cast<const f32x4*>(o + j);
+        }
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int j = wj * 128 + jb * 32 + g * 8 + lh;
+          if (j >= j_valid) continue;
+          const f32x16& a = acc[ib][jb];
+          f32x4 v = old[jb][g];
+          // One IEEE fp32 add per element of the finished product (no contraction).
+          v[0] = __fadd_rn(v[0], a[4 * g + 0]);
+          v[1] = __fadd_rn(v[1], a[4 * g + 1]);
+          v[2] = __fadd_rn(v[2], a[4 * g + 2]);
+          v[3] = __fadd_rn(v[3], a[4 * g + 3]);
+          *reinterpret_cast<f32x4*>(o + j) = v;
+        }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
+// one unit of work, decoded
+// ---------------------------------------------------------------------------
+struct Unit {
+  int valid;
+  int nk;        // reduction stages of 32, rounded up to a multiple of 4 (extra stages load zeros)
+  Operand a, b;
+  void* out;
+  int64_t ldc;
+  int i_valid, j_valid, mode;
+};
+
+template <int OP>
+__device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTable& tb, const UnitShape& us,
+                                            int total, int u) {
+  Unit x;
+  x.valid = u < total;
+  if (!x.valid) return x;
+  const int E = p.num_groups;
+  const int N = p.n, K = p.k;
+  const int e = uniform(find_group(tb.uprefix, E, u));
+  const int gs = uniform(e == 0 ? 0 : tb.end[e - 1]);
+  const int gm = uniform(tb.end[e]) - gs;
+  const int ul = u - uniform(tb.uprefix[e]);
+  const uint8_t* A = reinterpret_cast<const uint8_t*>(p.a);
+  const uint8_t* B = reinterpret_cast<const uint8_t*>(p.b);
+  const int64_t M = p.m_rows;
+  x.mode = kStoreBf16;
+  if (OP == kFwd || OP == kDgrad) {
+    int rt, ct;
+    panel_order(ul, (gm + kTileI - 1) / kTileI, us.n_j, 4, &rt, &ct);
+    const int row0 = gs + rt * kTileI;
+    x.i_valid = min(kTileI, gm - rt * kTileI);
+    const int j0 = ct * kTileJ;
+    x.nk = ((OP == kFwd ? K : N) / kTileR + 3) & ~3;
+    if (OP == kFwd) {
+      x.a = Operand{A + (int64_t)row0 * K * 2, A + M * K * 2, K * 2, x.i_valid, K};         // X rows
+      x.b = Operand{B + ((int64_t)e * N + j0) * K * 2, B + (int64_t)E * N * K * 2, K * 2,  // W[e] rows n
+                    kTileJ, K};
+      x.j_valid = kTileJ;
+      x.out = static_cast<uint16_t*>(p.out) + (int64_t)row0 * N + j0;
+      x.ldc = N;
+    } else {
+      x.a = Operand{A + (int64_t)row0 * N * 2, A + M * N * 2, N * 2, x.i_valid, N};         // G rows
+      x.b = Operand{B + ((int64_t)e * N * K + j0) * 2, B + (int64_t)E * N * K * 2, K * 2,  // W[e] columns k
+                    N, 0};
+      x.j_valid = min(kTileJ, K - j0);
+      x.out = static_cast<uint16_t*>(p.out) + (int64_t)row0 * K + j0;
+      x.ldc = K;
+    }
+  } else {
+    const int tiles = us.n_i * us.n_j;
+    const int c = ul / tiles;
+    int ti, tj;
+    panel_order(ul - c * tiles, us.n_i, us.n_j, 4, &ti, &tj);
+    const int R = p.chunk_rows;
+    const int r_start = gs + c * R;
+    int red = min(R, gm - c * R);
+    red = red < 0 ? 0 : red;
+    const int i0 = ti * kTileI, j0 = tj * kTileJ;
+    x.a = Operand{A + ((int64_t)r_start * N + i0) * 2, A + M * N * 2, N * 2, red, 0};  // G rows, columns n
+    x.b = Operand{B + ((int64_t)r_start * K + j0) * 2, B + M * K * 2, K * 2, red, 0};  // X rows, columns k
+    x.nk = ((red + kTileR - 1) / kTileR + 3) & ~3;
+    x.i_valid = kTileI;
+    x.j_valid = min(kTileJ, K - j0);
+    x.ldc = K;
+    const int chunks = group_slices<kWgrad>(gm, p);
+    if (chunks > 1) {
+      const int slot = uniform(tb.sprefix[e]) + c;
+      x.out = p.partial + (int64_t)slot * N * K + (int64_t)i0 * K + j0;
+      x.mode = kStoreF32;
+    } else if (p.out_fp32) {
+      x.out = static_cast<float*>(p.out) + (int64_t)e * N * K + (int64_t)i0 * K + j0;
+      x.mode = p.accumulate ? kStoreF32Acc : kStoreF32;
+    } else {
+      x.out = static_cast<uint16_t*>(p.out) + (int64_t)e * N * K + (int64_t)i0 * K + j0;
+      x.mode = kStoreBf16;
+    }
+  }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
 // the GEMM kernel
 // ---------------------------------------------------------------------------
+// The LDS stage ring: one separate array per (stage buffer, operand).  Distinct
+// objects let the compiler prove that reading one buffer does not depend on the
+// loads still landing in the others, so it never waits for the whole load queue
+// before an LDS read.
+__shared__ __attribute__((aligned(1024))) uint8_t s_a0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_a1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_a2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_a3[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_b0[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_b1[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_b2[kStageBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t s_b3[kStageBytes];
+
+template <int S>
+__device__ __forceinline__ uint8_t* stage_a() {
+  if constexpr (S == 0) return s_a0;
+  else if constexpr (S == 1) return s_a1;
+  else if constexpr (S == 2) return s_a2;
+  else return s_a3;
+}
+template <int S>
+__device__ __forceinline__ uint8_t* stage_b() {
+  if constexpr (S == 0) return s_b0;
+  else if constexpr (S == 1) return s_b1;
+  else if constexpr (S == 2) return s_b2;
+  else return s_b3;
+}
+
+template <int OP>
+struct Pipe {
+  static constexpr bool ATC = (OP == kWgrad);
+  static constexpr bool BTC = (OP != kFwd);
+  uint32_t off_a[4], off_b[4];
+  int w, wi, wj, lane;
+
+  template <int S>
+  __device__ __forceinline__ void issue(const Unit& x, int kt) const {
+    dma_stage<ATC>(x.a, off_a, stage_a<S>(), kt, w);
+    dma_stage<BTC>(x.b, off_b, stage_b<S>(), kt, w);
+  }
+
+  // Stages 0..2 of a unit, into buffers 0..2.
+  __device__ __forceinline__ void prefetch(const Unit& x) const {
+    if (x.nk > 0) issue<0>(x, 0);
+    if (x.nk > 1) issue<1>(x, 1);
+    if (x.nk > 2) issue<2>(x, 2);
+  }
+
+  // Stage kt, held in buffer S = kt % 4.  On entry the fragments of its first
+  // half are in (fa0, fb0).  Issues stage kt+3, runs the first half's MFMAs
+  // while reading the second half, waits for stage kt+1 and passes the barrier,
+  // then runs the second half's MFMAs while reading stage kt+1's first half.
+  template <int S>
+  __device__ __forceinline__ void step(f32x16 (&acc)[4][4], bf16x8 (&fa0)[4], bf16x8 (&fb0)[4],
+                                       bf16x8 (&fa1)[4], bf16x8 (&fb1)[4], const Unit& x, int kt) const {
+    constexpr int S1 = (S + 1) & 3, S3 = (S + 3) & 3;
+    if (kt + 3 < x.nk) issue<S3>(x, kt + 3);
+    mma_16_with_reads<ATC, BTC>(acc, fa0, fb0, fa1, fb1, stage_a<S>(), stage_b<S>(), wi, wj, 1, lane);
+    if (kt + 1 < x.nk) {
+      wait_stage(min(kStages - 2, x.nk - 2 - kt));  // stages issued after kt+1 may stay in flight
+      lds_barrier();  // stage kt+1 visible; stage kt's reads all returned
+    }
+    // (after the last stage these reads are discarded)
+    mma_16_with_reads<ATC, BTC>(acc, fa1, fb1, fa0, fb0, stage_a<S1>(), stage_b<S1>(), wi, wj, 0, lane);
+  }
+};
+
+// Per unit, with stages of 32 reductions in a ring of 4 LDS buffers:
+//   * stages 0..2 are loaded ahead (for every unit but the first, during the
+//     previous unit's epilogue);
+//   * stage kt: issue stage kt+3 into the buffer stage kt-1 used; read the
+//     second half of stage kt's fragments while the MFMAs of its first half
+//     run; wait for stage kt+1 and pass one barrier; read the first half of
+//     stage kt+1's fragments while the MFMAs of stage kt's second half run.
+// One barrier per stage, and no MFMA waits on an LDS read.
 template <int OP>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2][kLdsTile];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[2][kLdsTile];
+  constexpr bool ATC = (OP == kWgrad);
+  constexpr bool BTC = (OP != kFwd);
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
@@ -375,82 +656,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const UnitShape us = unit_shape<OP>(p);
 
   const int P = gridDim.x;
-  const int b = blockIdx.x;
-  const int vb = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wi = w >> 1, wj = w & 1;
-  const int E = p.num_groups;
-  const int N = p.n, K = p.k;
+  const int bid = blockIdx.x;
+  const int vb = (P % 8 == 0) ? (bid % 8) * (P / 8) + bid / 8 : bid;
 
-  for (int u = vb; u < total; u += P) {
-    const int e = find_group(s_uprefix, E, u);
-    const int gs = (e == 0) ? 0 : s_end[e - 1];
-    const int gm = s_end[e] - gs;
-    const int ul = u - s_uprefix[e];
+  Pipe<OP> pipe;
+  pipe.lane = threadIdx.x & 63;
+  pipe.w = threadIdx.x >> 6;
+  pipe.wi = pipe.w >> 1;
+  pipe.wj = pipe.w & 1;
+  // DMA offsets depend only on the operands' row strides (fixed per launch).
+  dma_offsets<ATC>(pipe.off_a, (OP == kFwd ? p.k : p.n) * 2, pipe.w, pipe.lane);
+  dma_offsets<BTC>(pipe.off_b, p.k * 2, pipe.w, pipe.lane);
 
-    // Unit geometry.
-    const uint16_t* a_base;
-    const uint16_t* b_base;
-    int a_ld, b_ld, nk, i_valid, j_valid, red_valid = 0;
-    void* out;
-    int64_t ldc;
-    int mode = kStoreBf16;
-    if (OP == kFwd || OP == kDgrad) {
-      int rt, ct;
-      panel_order(ul, (gm + kTileI - 1) / kTileI, us.n_j, 4, &rt, &ct);
-      const int row0 = gs + rt * kTileI;
-      i_valid = min(kTileI, gm - rt * kTileI);
-      const int j0 = ct * kTileJ;
-      if (OP == kFwd) {
-        a_base = p.a + (size_t)row0 * K;                          // X rows
-        a_ld = K;
-        b_base = p.b + ((size_t)e * N + j0) * K;                  // W[e] rows n
-        b_ld = K;
-        nk = K / kTileR;
-        j_valid = kTileJ;
-        out = static_cast<uint16_t*>(p.out) + (size_t)row0 * N + j0;
-        ldc = N;
-      } else {
-        a_base = p.a + (size_t)row0 * N;                          // G rows
-        a_ld = N;
-        b_base = p.b + (size_t)e * N * K + j0;                    // W[e] columns k
-        b_ld = K;
-        nk = N / kTileR;
-        j_valid = min(kTileJ, K - j0);
-        out = static_cast<uint16_t*>(p.out) + (size_t)row0 * K + j0;
-        ldc = K;
-      }
-    } else {
-      const int tiles = us.n_i * us.n_j;
-      const int c = ul / tiles;
-      int ti, tj;
-      panel_order(ul - c * tiles, us.n_i, us.n_j, 4, &ti, &tj);
-      const int R = p.chunk_rows;
-      const int r_start = gs + c * R;
-      red_valid = min(R, gm - c * R);
-      if (red_valid < 0) red_valid = 0;
-      const int i0 = ti * kTileI, j0 = tj * kTileJ;
-      a_base = p.a + (size_t)r_start * N + i0;                    // G rows, columns n
-      a_ld = N;
-      b_base = p.b + (size_t)r_start * K + j0;                    // X rows, columns k
-      b_ld = K;
-      nk = (red_valid + kTileR - 1) / kTileR;
-      i_valid = kTileI;
-      j_valid = min(kTileJ, K - j0);
-      const int chunks = group_slices<kWgrad>(gm, p);
-      ldc = K;
-      if (chunks > 1) {
-        out = p.partial + (size_t)(s_sprefix[e] + c) * N * K + (size_t)i0 * K + j0;
-        mode = kStoreF32;
-      } else if (p.out_fp32) {
-        out = static_cast<float*>(p.out) + (size_t)e * N * K + (size_t)i0 * K + j0;
-        mode = p.accumulate ? kStoreF32Acc : kStoreF32;
-      } else {
-        out = static_cast<uint16_t*>(p.out) + (size_t)e * N * K + (size_t)i0 * K + j0;
-        mode = kStoreBf16;
-      }
-    }
-
+  Unit cur = decode_unit<OP>(p, tb, us, total, vb);
+  if (cur.valid) pipe.prefetch(cur);
+  for (int u = vb; cur.valid; u += P) {
     f32x16 acc[4][4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
@@ -459,38 +679,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int x = 0; x < 16; ++x) acc[ib][jb][x] = 0.0f;
 
-    if (nk > 0) {
-      // A operand: fwd/dgrad rows of the group (reduction contiguous);
-      // wgrad G^T (reduction strided).  B operand: fwd W[e] (reduction
-      // contiguous); dgrad W[e] and wgrad X (reduction strided).
-      LoadRC la_rc, lb_rc;
-      LoadTC la_tc, lb_tc;
-      auto load = [&](int kt) {
-        const int r0 = kt * kTileR;
-        if (OP == kWgrad) la_tc.load(a_base, a_ld, red_valid, kTileI, r0);
-        else la_rc.load(a_base, a_ld, i_valid, r0);
-        if (OP == kFwd) lb_rc.load(b_base, b_ld, kTileJ, r0);
-        else lb_tc.load(b_base, b_ld, OP == kWgrad ? red_valid : N, j_valid, r0);
-      };
-      auto stage = [&](int buf) {
-        if (OP == kWgrad) la_tc.store(s_a[buf]);
-        else la_rc.store(s_a[buf]);
-        if (OP == kFwd) lb_rc.store(s_b[buf]);
-        else lb_tc.store(s_b[buf]);
-      };
-      load(0);
-      stage(0);
-      __syncthreads();
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) load(kt + 1);
-        mma_step(acc, s_a[cur], s_b[cur], wi, wj, lane);
-        if (kt + 1 < nk) stage(cur ^ 1);
-        __syncthreads();
+    if (cur.nk > 0) {
+      bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+      wait_stage(min(kStages - 2, cur.nk - 1));
+      lds_barrier();  // stage 0 visible
+      load_frags<ATC, BTC>(fa0, fb0, stage_a<0>(), stage_b<0>(), pipe.wi, pipe.wj, 0, pipe.lane);
+      for (int kt = 0; kt < cur.nk; kt += 4) {
+        pipe.template step<0>(acc, fa0, fb0, fa1, fb1, cur, kt);
+        pipe.template step<1>(acc, fa0, fb0, fa1, fb1, cur, kt + 1);
+        pipe.template step<2>(acc, fa0, fb0, fa1, fb1, cur, kt + 2);
+        pipe.template step<3>(acc, fa0, fb0, fa1, fb1, cur, kt + 3);
       }
     }
-    store_tile(acc, out, ldc, i_valid, j_valid, wi, wj, lane, mode);
+    wait_vm_lgkm<0>();
+    __syncthreads();  // every wave is done reading LDS before the next unit's loads
+    const Unit nxt = decode_unit<OP>(p, tb, us, total, u + P);
+    if (nxt.valid) pipe.prefetch(nxt);
+    store_tile(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane, cur.mode);
+    cur = nxt;
   }
+  wait_vm_lgkm<0>();
 }
 
 // ---------------------------------------------------------------------------
