@@ -266,46 +266,40 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int ld_bytes, in
   }
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const uint8_t* base, int64_t bytes) {
-  if (bytes < 0) bytes = 0;
-  if (bytes > 0x7FFFFFF0) bytes = 0x7FFFFFF0;
-  // word 3: 32-bit data format, raw (unswizzled) addressing
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, (int)bytes, 0x00020000);
-}
-
-// Operand of one unit: where its data starts and how much of it is real.
+// Operand of one unit: where its data starts and how much of it is real.  The
+// byte ranges handed to the buffer loads never leave the operand's own valid
+// rows, so no load can touch memory past a tensor.
 struct Operand {
   const uint8_t* base;  // element (first row, first column) of the unit's panel
-  const uint8_t* end;   // one past the tensor's last byte (memory-safety clip)
   int ld_bytes;         // row stride in memory
-  int rows_valid;       // RC: valid rows of the 256-row panel; TC: valid reduction rows
-  int red_len;          // RC: reduction extent (stages at or past it load zeros)
+  int lim;              // RC: bytes of the valid rows (rows_valid * ld_bytes); TC: valid reduction rows
+  int aux;              // RC: reduction extent in bytes; TC: valid bytes of a row (valid columns * 2)
 };
 
-// Issues this wave's DMA loads of reduction stage `kt` of one operand.  The
-// buffer's range check zero-fills everything past the valid rows.
+// Issues this wave's DMA loads of reduction stage `kt` of one operand into the
+// LDS stage at `lds` (a wave-uniform address: `lds_w` already includes this
+// wave's first segment).  The buffer's range check zero-fills everything past
+// the valid rows (and, for RC operands, stages past the reduction extent).
 template <bool TC>
-__device__ __forceinline__ void dma_stage(const Operand& o, const uint32_t (&off)[4], uint8_t* lds_stage,
-                                          int kt, int w) {
+__device__ __forceinline__ void dma_stage(const Operand& o, const uint32_t (&off)[4], uint8_t* lds_w, int kt,
+                                          bool live) {
   const int r0 = kt * kTileR;
   const uint8_t* base;
-  int64_t bytes;
+  int bytes;
   if (!TC) {
-    base = o.base + (int64_t)r0 * 2;
-    bytes = r0 < o.red_len ? (int64_t)o.rows_valid * o.ld_bytes - (int64_t)r0 * 2 : 0;
+    base = o.base + r0 * 2;
+    bytes = r0 * 2 < o.aux ? o.lim - r0 * 2 : 0;
   } else {
     base = o.base + (int64_t)r0 * o.ld_bytes;
-    int rows = o.rows_valid - r0;
-    rows = rows < 0 ? 0 : (rows > kTileR ? kTileR : rows);
-    bytes = (int64_t)rows * o.ld_bytes;
+    const int rows = min(max(o.lim - r0, 0), kTileR);
+    bytes = rows > 0 ? (rows - 1) * o.ld_bytes + o.aux : 0;
   }
-  const int64_t left = o.end - base;
-  if (bytes > left) bytes = left;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, bytes);
+  if (!live) bytes = 0;  // a stage past the unit's last one: the loads only write zeros
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_stage + (q * 4 + w) * 1024), 16, off[q], 0, 0,
-                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_w + q * 4096), 16, off[q], 0, 0, 0);
 }
 
 // Waits until at most `kVm` of this wave's vector memory operations are
@@ -329,13 +323,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 // DMA loads per stage per wave (both operands).
 constexpr int kDmaPerStage = 8;
-
-// Waits for stage `next` when `ahead` later stages may still be in flight.
-__device__ __forceinline__ void wait_stage(int ahead) {
-  if (ahead >= 2) wait_vm_lgkm<2 * kDmaPerStage>();
-  else if (ahead == 1) wait_vm_lgkm<kDmaPerStage>();
-  else wait_vm_lgkm<0>();
-}
 
 // ---------------------------------------------------------------------------
 // MFMA fragments from LDS
@@ -508,7 +495,6 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
   const int ul = u - uniform(tb.uprefix[e]);
   const uint8_t* A = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* B = reinterpret_cast<const uint8_t*>(p.b);
-  const int64_t M = p.m_rows;
   x.mode = kStoreBf16;
   if (OP == kFwd || OP == kDgrad) {
     int rt, ct;
@@ -518,16 +504,14 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     const int j0 = ct * kTileJ;
     x.nk = ((OP == kFwd ? K : N) / kTileR + 3) & ~3;
     if (OP == kFwd) {
-      x.a = Operand{A + (int64_t)row0 * K * 2, A + M * K * 2, K * 2, x.i_valid, K};         // X rows
-      x.b = Operand{B + ((int64_t)e * N + j0) * K * 2, B + (int64_t)E * N * K * 2, K * 2,  // W[e] rows n
-                    kTileJ, K};
+      x.a = Operand{A + (int64_t)row0 * K * 2, K * 2, x.i_valid * K * 2, K * 2};        // X rows
+      x.b = Operand{B + ((int64_t)e * N + j0) * K * 2, K * 2, kTileJ * K * 2, K * 2};  // W[e] rows n
       x.j_valid = kTileJ;
       x.out = static_cast<uint16_t*>(p.out) + (int64_t)row0 * N + j0;
       x.ldc = N;
     } else {
-      x.a = Operand{A + (int64_t)row0 * N * 2, A + M * N * 2, N * 2, x.i_valid, N};         // G rows
-      x.b = Operand{B + ((int64_t)e * N * K + j0) * 2, B + (int64_t)E * N * K * 2, K * 2,  // W[e] columns k
-                    N, 0};
+      x.a = Operand{A + (int64_t)row0 * N * 2, N * 2, x.i_valid * N * 2, N * 2};         // G rows
+      x.b = Operand{B + ((int64_t)e * N * K + j0) * 2, K * 2, N, min(kTileJ, K - j0) * 2};  // W[e] columns k
       x.j_valid = min(kTileJ, K - j0);
       x.out = static_cast<uint16_t*>(p.out) + (int64_t)row0 * K + j0;
       x.ldc = K;
@@ -542,8 +526,8 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     int red = min(R, gm - c * R);
     red = red < 0 ? 0 : red;
     const int i0 = ti * kTileI, j0 = tj * kTileJ;
-    x.a = Operand{A + ((int64_t)r_start * N + i0) * 2, A + M * N * 2, N * 2, red, 0};  // G rows, columns n
-    x.b = Operand{B + ((int64_t)r_start * K + j0) * 2, B + M * K * 2, K * 2, red, 0};  // X rows, columns k
+    x.a = Operand{A + ((int64_t)r_start * N + i0) * 2, N * 2, red, kTileI * 2};                  // G rows, columns n
+    x.b = Operand{B + ((int64_t)r_start * K + j0) * 2, K * 2, red, min(kTileJ, K - j0) * 2};  // X rows, columns k
     x.nk = ((red + kTileR - 1) / kTileR + 3) & ~3;
     x.i_valid = kTileI;
     x.j_valid = min(kTileJ, K - j0);
@@ -604,31 +588,43 @@ struct Pipe {
 
   template <int S>
   __device__ __forceinline__ void issue(const Unit& x, int kt) const {
-    dma_stage<ATC>(x.a, off_a, stage_a<S>(), kt, w);
-    dma_stage<BTC>(x.b, off_b, stage_b<S>(), kt, w);
+    const bool live = kt < x.nk;
+    dma_stage<ATC>(x.a, off_a, stage_a<S>() + w * 1024, kt, live);
+    dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, live);
   }
 
   // Stages 0..2 of a unit, into buffers 0..2.
   __device__ __forceinline__ void prefetch(const Unit& x) const {
-    if (x.nk > 0) issue<0>(x, 0);
-    if (x.nk > 1) issue<1>(x, 1);
-    if (x.nk > 2) issue<2>(x, 2);
+    issue<0>(x, 0);
+    issue<1>(x, 1);
+    issue<2>(x, 2);
   }
 
   // Stage kt, held in buffer S = kt % 4.  On entry the fragments of its first
-  // half are in (fa0, fb0).  Issues stage kt+3, runs the first half's MFMAs
-  // while reading the second half, waits for stage kt+1 and passes the barrier,
-  // then runs the second half's MFMAs while reading stage kt+1's first half.
+  // half are in (fa0, fb0).  Issues stage kt+3 (zeros past the last stage),
+  // runs the first half's MFMAs while reading the second half, waits for stage
+  // kt+1 and passes the barrier, then runs the second half's MFMAs while
+  // reading stage kt+1's first half.  Branch-free: every step issues the same
+  // loads, so the wait counts are constants and the step is one scheduling
+  // region in which the loads, LDS reads and MFMAs interleave.
   template <int S>
   __device__ __forceinline__ void step(f32x16 (&acc)[4][4], bf16x8 (&fa0)[4], bf16x8 (&fb0)[4],
                                        bf16x8 (&fa1)[4], bf16x8 (&fb1)[4], const Unit& x, int kt) const {
     constexpr int S1 = (S + 1) & 3, S3 = (S + 3) & 3;
-    if (kt + 3 < x.nk) issue<S3>(x, kt + 3);
-    mma_16_with_reads<ATC, BTC>(acc, fa0, fb0, fa1, fb1, stage_a<S>(), stage_b<S>(), wi, wj, 1, lane);
-    if (kt + 1 < x.nk) {
-      wait_stage(min(kStages - 2, x.nk - 2 - kt));  // stages issued after kt+1 may stay in flight
-      lds_barrier();  // stage kt+1 visible; stage kt's reads all returned
+    constexpr int kReads = 4 * (ATC ? 2 : 1) + 4 * (BTC ? 2 : 1);
+    load_frags<ATC, BTC>(fa1, fb1, stage_a<S>(), stage_b<S>(), wi, wj, 1, lane);
+    issue<S3>(x, kt + 3);
+    mma_16(acc, fa0, fb0);
+    // interleave: 16 MFMAs with the reads of the second half and the 8 loads
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
+    wait_vm_lgkm<2 * kDmaPerStage>();  // stage kt+1 has landed (kt+2, kt+3 may be in flight)
+    lds_barrier();                      // ... in every wave; stage kt's reads all returned
     // (after the last stage these reads are discarded)
     mma_16_with_reads<ATC, BTC>(acc, fa1, fb1, fa0, fb0, stage_a<S1>(), stage_b<S1>(), wi, wj, 0, lane);
   }
@@ -661,7 +657,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
   Pipe<OP> pipe;
   pipe.lane = threadIdx.x & 63;
-  pipe.w = threadIdx.x >> 6;
+  pipe.w = uniform(threadIdx.x >> 6);
   pipe.wi = pipe.w >> 1;
   pipe.wj = pipe.w & 1;
   // DMA offsets depend only on the operands' row strides (fixed per launch).
@@ -681,7 +677,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
     if (cur.nk > 0) {
       bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-      wait_stage(min(kStages - 2, cur.nk - 1));
+      wait_vm_lgkm<2 * kDmaPerStage>();
       lds_barrier();  // stage 0 visible
       load_frags<ATC, BTC>(fa0, fb0, stage_a<0>(), stage_b<0>(), pipe.wi, pipe.wj, 0, pipe.lane);
       for (int kt = 0; kt < cur.nk; kt += 4) {
