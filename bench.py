@@ -40,7 +40,50 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 times): the reference kernel "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib: int) -> None:
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "reps": 5}), flush=True)
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "moe_ragged_bf16_amd", "csrc", "grouped_gemm_kernels.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3
+    PMC summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel), or None
+    if there is none or the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(d, target_s: float):
@@ -97,6 +140,9 @@ def cpu_baseline(d, target_s: float):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU runs are not part of this build.", file=sys.stderr)
@@ -179,11 +225,22 @@ def main():
     # dominant kernel: the op with the largest average launch time
     dom = max(op_ms, key=op_ms.get)
     achieved = flop_op / (op_ms[dom] * 1e-3) / 1e12
-    traffic = None
+    # algorithmic HBM bytes per launch: each operand read once, outputs written once
+    # (W only for non-empty experts; main_grad read and written by the accumulate)
+    alg_bytes = {
+        "fwd": 2 * (M * K + e_ne * N * K + M * N),
+        "dgrad": 2 * (M * N + e_ne * N * K + M * K),
+        "wgrad_fp32_accumulate": 2 * (M * N + M * K) + 8 * E * N * K,
+    }
+    kernel_name = {"fwd": "fwd", "dgrad": "dgrad", "wgrad_fp32_accumulate": "wgrad"}[dom]
+    traffic = measured_traffic(args.workload, kernel_name)
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic, "kernel": dom,
-                "flops_per_launch": flop_op}
+                "flops_per_launch": flop_op,
+                "algorithmic_bytes_per_launch": alg_bytes[dom],
+                "arithmetic_intensity": round(flop_op / alg_bytes[dom], 1),
+                "hbm_gbs_at_algorithmic_bytes": round(alg_bytes[dom] / (op_ms[dom] * 1e-3) / 1e9, 1)}
 
     cpu = None
     if not args.no_cpu_baseline:
