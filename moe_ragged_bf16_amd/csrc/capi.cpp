@@ -9,6 +9,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "grouped_gemm.h"
@@ -46,9 +47,36 @@ int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_
   return big == 0 ? 0 : m_rows / chunk_rows + big;
 }
 
+// Row length of the packed transposed copies: every group padded to kGroupPad
+// rows (sum of padded sizes <= M + (kGroupPad - 1) * E), rounded up to 64.
+int64_t wgrad_packed_ld(int64_t m_rows, int32_t num_groups) {
+  const int64_t rows = m_rows + (int64_t)(kGroupPad - 1) * num_groups;
+  return (rows + 63) / 64 * 64;
+}
+
 namespace {
 
 constexpr size_t kTableBytes = 4096;  // reserved head of the workspace
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Workspace regions of wgrad, in order: reserved head, fp32 partial tiles of
+// split experts, G^T and X^T packed copies.
+struct WgradWorkspace {
+  size_t partial_off, gt_off, xt_off, total;
+};
+
+WgradWorkspace wgrad_workspace(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  WgradWorkspace w;
+  const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
+  const int64_t slots = wgrad_max_partial_slots(m_rows, r, num_groups);
+  const int64_t ldp = wgrad_packed_ld(m_rows, num_groups);
+  w.partial_off = kTableBytes;
+  w.gt_off = align256(w.partial_off + (size_t)slots * (size_t)n * (size_t)k * sizeof(float));
+  w.xt_off = align256(w.gt_off + (size_t)n * (size_t)ldp * 2);
+  w.total = align256(w.xt_off + (size_t)k * (size_t)ldp * 2);
+  return w;
+}
 
 struct DeviceInfo {
   bool ok = false;
@@ -97,7 +125,7 @@ int check_sizes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (m_rows < 0 || n <= 0 || k <= 0 || num_groups <= 0) return MDG_EINVAL;
   if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
   if (n % kTileI != 0 || k % kKAlign != 0) return MDG_EUNSUPPORTED;
-  if (m_rows > INT32_MAX / 2 || n > (1 << 20) || k > (1 << 20) || n * k > INT32_MAX)
+  if (m_rows > kMaxRows || n > (1 << 20) || k > (1 << 20) || n * k > INT32_MAX)
     return MDG_EUNSUPPORTED;
   return MDG_OK;
 }
@@ -184,9 +212,7 @@ int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, 
 
 size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
-  const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
-  const int64_t slots = wgrad_max_partial_slots(m_rows, r, num_groups);
-  return kTableBytes + (size_t)slots * (size_t)n * (size_t)k * sizeof(float);
+  return wgrad_workspace(m_rows, n, k, num_groups).total;
 }
 
 int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
@@ -218,12 +244,17 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
   if (!dev.gfx950) return MDG_EUNSUPPORTED;
 
   const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
+  const WgradWorkspace wl = wgrad_workspace(m_rows, n, k, num_groups);
+  char* ws = static_cast<char*>(workspace);
   GemmParams p{};
   p.a = static_cast<const uint16_t*>(g);
   p.b = static_cast<const uint16_t*>(x);
   p.offs = offs;
   p.out = dw;
-  p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + kTableBytes);
+  p.partial = reinterpret_cast<float*>(ws + wl.partial_off);
+  p.gt = reinterpret_cast<const uint16_t*>(ws + wl.gt_off);
+  p.xt = reinterpret_cast<const uint16_t*>(ws + wl.xt_off);
+  p.ldp = wgrad_packed_ld(m_rows, num_groups);
   p.m_rows = m_rows;
   p.n = (int32_t)n;
   p.k = (int32_t)k;
@@ -236,6 +267,15 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
   const int64_t units_ub = tiles * (num_groups + m_rows / r);
   if (units_ub > INT32_MAX) return MDG_EUNSUPPORTED;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (m_rows > 0) {
+    // G^T and X^T packed copies (rows of each group contiguous, zero-padded)
+    const int64_t ptiles = p.ldp / 64;
+    const int pgrid = (int)std::min<int64_t>(4 * (int64_t)(dev.cus > 0 ? dev.cus : 256), ptiles * ((n > k ? n : k) / 64));
+    PackParams qg{p, static_cast<const uint16_t*>(g), reinterpret_cast<uint16_t*>(ws + wl.gt_off), (int32_t)n};
+    PackParams qx{p, static_cast<const uint16_t*>(x), reinterpret_cast<uint16_t*>(ws + wl.xt_off), (int32_t)k};
+    if (launch_wgrad_pack(qg, pgrid, s) != hipSuccess) return MDG_EHIP;
+    if (launch_wgrad_pack(qx, pgrid, s) != hipSuccess) return MDG_EHIP;
+  }
   if (launch_gemm(kWgrad, p, persistent_grid(units_ub, dev.cus), s) != hipSuccess) return MDG_EHIP;
   const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
   if (split_ub > 0) {

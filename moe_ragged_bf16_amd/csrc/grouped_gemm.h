@@ -17,6 +17,8 @@ constexpr int kKAlign = 64;      // k must be a multiple of this (the ABI's cont
 constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
+constexpr int kGroupPad = 32;    // wgrad: each group's rows are zero-padded to a multiple of this
+constexpr int64_t kMaxRows = 4000000;  // m_rows limit (keeps the packed layout's buffer ranges < 2^31)
 
 enum Op : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
@@ -31,15 +33,29 @@ struct GemmParams {
   int32_t chunk_rows;     // wgrad rows per chunk
   int32_t out_fp32;       // wgrad: dW is fp32
   int32_t accumulate;     // wgrad: dW = RN32(dW + product)
+  const uint16_t* gt;     // wgrad: G^T [n, ldp], groups zero-padded to kGroupPad rows (workspace)
+  const uint16_t* xt;     // wgrad: X^T [k, ldp], same layout (workspace)
+  int64_t ldp;            // wgrad: row length of gt / xt (elements)
+};
+
+// wgrad pack: dst[c][P_e + r] = src[s_e + r][c] for r < m_e, 0 up to the padded
+// group end (P_e = sum of the padded sizes of the groups before e).
+struct PackParams {
+  GemmParams g;           // offs, m_rows, num_groups, ldp (the rest unused)
+  const uint16_t* src;    // [m_rows, cols] bf16
+  uint16_t* dst;          // [cols, ldp] bf16
+  int32_t cols;           // multiple of 64
 };
 
 // Launchers (grouped_gemm_kernels.hip).  Return the HIP status of the launch.
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
+hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream);
 
 // Host-side sizing helpers (capi.cpp).
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);
 int64_t wgrad_max_split_groups(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
 int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
+int64_t wgrad_packed_ld(int64_t m_rows, int32_t num_groups);
 
 }  // namespace mdg

@@ -51,6 +51,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -146,6 +147,7 @@ struct GroupTable {
   int* end;      // [E]     clamped, non-decreasing end row of each group
   int* uprefix;  // [E + 1] exclusive prefix of work units
   int* sprefix;  // [E]     wgrad: exclusive prefix of partial slots (split groups only)
+  int* pprefix;  // [E + 1] wgrad: exclusive prefix of the group sizes padded to kGroupPad
   int* scratch;  // [4]
 };
 
@@ -168,8 +170,8 @@ __device__ int build_group_table(const GemmParams& p, GroupTable tb) {
     endv[q] = run;
   }
   const int before = block_excl_max(run, tb.scratch);
-  int units[4], slots[4];
-  int usum = 0, ssum = 0;
+  int units[4], slots[4], pads[4];
+  int usum = 0, ssum = 0, psum = 0;
   int start = before;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -178,30 +180,39 @@ __device__ int build_group_table(const GemmParams& p, GroupTable tb) {
     const int m = end - start;
     units[q] = 0;
     slots[q] = 0;
+    pads[q] = 0;
     if (e < E) {
       const int sl = group_slices<OP>(m, p);
       units[q] = sl * tiles_per_slice;
       slots[q] = (OP == kWgrad && sl > 1) ? sl : 0;
+      pads[q] = (m + kGroupPad - 1) / kGroupPad * kGroupPad;
       tb.end[e] = end;
     }
     usum += units[q];
     ssum += slots[q];
+    psum += pads[q];
     start = end;
   }
-  int utotal, stotal;
+  int utotal, stotal, ptotal;
   int ub = block_excl_sum(usum, tb.scratch, &utotal);
   int sb = block_excl_sum(ssum, tb.scratch, &stotal);
+  int pb = OP == kWgrad ? block_excl_sum(psum, tb.scratch, &ptotal) : 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * t + q;
     if (e < E) {
       tb.uprefix[e] = ub;
       tb.sprefix[e] = sb;
+      if (OP == kWgrad) tb.pprefix[e] = pb;
     }
     ub += units[q];
     sb += slots[q];
+    pb += pads[q];
   }
-  if (t == 0) tb.uprefix[E] = utotal;
+  if (t == 0) {
+    tb.uprefix[E] = utotal;
+    if (OP == kWgrad) tb.pprefix[E] = ptotal;
+  }
   __syncthreads();
   return utotal;
 }
@@ -404,67 +415,93 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Epilogue store modes.
 enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2 };
 
-// Writes this wave's accumulators to `out` (row stride ldc elements), rows
-// i < i_valid and columns j < j_valid of the 256 x 256 tile.
+// Byte offset that the buffer range check rejects: a load returns 0 and a store
+// is dropped.  Masked lanes use it, so every wave issues the same instructions.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Writes this wave's accumulators to the tile at `out` (row stride ldc
+// elements): rows i < i_valid and columns j < j_valid of the 256 x 256 tile
+// (j_valid is a multiple of 64, so a 32-column block is valid or not as a
+// whole).  All accesses are buffer operations on one descriptor covering the
+// tile's valid extent; masked lanes get an offset the range check turns away.
+// The fused accumulate reads the destination in chunks of 8 x 16 bytes per lane,
+// one chunk ahead of the chunk being added and stored (one IEEE fp32 add per
+// element, no contraction).
+template <int mode>
 __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out, int64_t ldc, int i_valid,
-                                           int j_valid, int wi, int wj, int lane, int mode) {
+                                           int j_valid, int wi, int wj, int lane) {
   const int lr = lane & 31, lh = (lane >> 5) * 4;
+  const int esz = mode == kStoreBf16 ? 2 : 4;
+  const int ldc_b = (int)ldc * esz;
+  const int extent = i_valid > 0 ? (i_valid - 1) * ldc_b + j_valid * esz : 0;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(out, 0, extent, 0x00020000);
+  const int base = (wi * 128 + lr) * ldc_b + (wj * 128 + lh) * esz;
+  // offset of row block ib, column block jb (the 8-column step g is added as an immediate)
+  auto voff = [&](int ib, int jb) -> uint32_t {
+    const bool ok = (wi * 128 + ib * 32 + lr) < i_valid && (wj * 128 + jb * 32) < j_valid;
+    return ok ? (uint32_t)(base + ib * 32 * ldc_b + jb * 32 * esz) : kOutOfRange;
+  };
+  if constexpr (mode == kStoreBf16) {
 #pragma unroll
-  for (int ib = 0; ib < 4; ++ib) {
-    const int i = wi * 128 + ib * 32 + lr;
-    if (i >= i_valid) continue;
-    if (mode == kStoreBf16) {
-      uint16_t* o = static_cast<uint16_t*>(out) + i * ldc;
+    for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint32_t o = voff(ib, jb);
+        const f32x16& a = acc[ib][jb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int j = wj * 128 + jb * 32 + g * 8 + lh;
-          if (j >= j_valid) continue;
-          const f32x16& a = acc[ib][jb];
           u32x2 pk;
           pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
           pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
-          *reinterpret_cast<u32x2*>(o + j) = pk;
+          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, o, g * 16, 0);
         }
-    } else if (mode == kStoreF32) {
-      float* o = static_cast<float*>(out) + i * ldc;
+      }
+  } else if constexpr (mode == kStoreF32) {
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const uint32_t o = voff(ib, jb);
+        const f32x16& a = acc[ib][jb];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int j = wj * 128 + jb * 32 + g * 8 + lh;
-          if (j >= j_valid) continue;
-          const f32x16& a = acc[ib][jb];
-          *reinterpret_cast<f32x4*>(o + j) = f32x4{a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, g * 32, 0);
         }
-    } else {
-      // Read-modify-write: all 16 reads of the row block are issued before the
-      // first add, so their latencies overlap.
-      float* o = static_cast<float*>(out) + i * ldc;
-      f32x4 old[4][4];
+      }
+  } else {
+    // chunk c = (ib, jb pair): 2 column blocks x 4 steps = 8 loads of 16 bytes
+    f32x4 cur[8], nxt[8];
+    auto load_chunk = [&](f32x4 (&dst)[8], int c) {
+      const int ib = c >> 1, jb0 = (c & 1) * 2;
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t o = voff(ib, jb0 + h);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dst[h * 4 + g] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, g * 32, 0);
+      }
+    };
+    load_chunk(cur, 0);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      if (c + 1 < 8) load_chunk(nxt, c + 1);
+      const int ib = c >> 1, jb0 = (c & 1) * 2;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t o = voff(ib, jb0 + h);
+        const f32x16& a = acc[ib][jb0 + h];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int j = wj * 128 + jb * 32 + g * 8 + lh;
-          if (j < j_valid) old[jb][g] = *reinterpret_cast<const f32x4*>(o + j);
-        }
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int j = wj * 128 + jb * 32 + g * 8 + lh;
-          if (j >= j_valid) continue;
-          const f32x16& a = acc[ib][jb];
-          f32x4 v = old[jb][g];
-          // One IEEE fp32 add per element of the finished product (no contraction).
+          f32x4 v = cur[h * 4 + g];
           v[0] = __fadd_rn(v[0], a[4 * g + 0]);
           v[1] = __fadd_rn(v[1], a[4 * g + 1]);
           v[2] = __fadd_rn(v[2], a[4 * g + 2]);
           v[3] = __fadd_rn(v[3], a[4 * g + 3]);
-          *reinterpret_cast<f32x4*>(o + j) = v;
+          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, g * 32, 0);
         }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
     }
   }
 }
@@ -522,15 +559,19 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     int ti, tj;
     panel_order(ul - c * tiles, us.n_i, us.n_j, 4, &ti, &tj);
     const int R = p.chunk_rows;
-    const int r_start = gs + c * R;
     int red = min(R, gm - c * R);
     red = red < 0 ? 0 : red;
+    const int red_pad = (red + kGroupPad - 1) / kGroupPad * kGroupPad;  // zeros past `red` in the packed copies
     const int i0 = ti * kTileI, j0 = tj * kTileJ;
-    x.a = Operand{A + ((int64_t)r_start * N + i0) * 2, N * 2, red, kTileI * 2};                  // G rows, columns n
-    x.b = Operand{B + ((int64_t)r_start * K + j0) * 2, K * 2, red, min(kTileJ, K - j0) * 2};  // X rows, columns k
-    x.nk = ((red + kTileR - 1) / kTileR + 3) & ~3;
-    x.i_valid = kTileI;
+    const int64_t col = uniform(tb.pprefix[e]) + (int64_t)c * R;        // first packed row of this chunk
+    const int ld_bytes = (int)(p.ldp * 2);
     x.j_valid = min(kTileJ, K - j0);
+    const uint8_t* GT = reinterpret_cast<const uint8_t*>(p.gt);
+    const uint8_t* XT = reinterpret_cast<const uint8_t*>(p.xt);
+    x.a = Operand{GT + ((int64_t)i0 * p.ldp + col) * 2, ld_bytes, kTileI * ld_bytes, red_pad * 2};      // G^T rows n
+    x.b = Operand{XT + ((int64_t)j0 * p.ldp + col) * 2, ld_bytes, x.j_valid * ld_bytes, red_pad * 2};  // X^T rows k
+    x.nk = ((red_pad / kTileR) + 3) & ~3;
+    x.i_valid = kTileI;
     x.ldc = K;
     const int chunks = group_slices<kWgrad>(gm, p);
     if (chunks > 1) {
@@ -581,8 +622,9 @@ __device__ __forceinline__ uint8_t* stage_b() {
 
 template <int OP>
 struct Pipe {
-  static constexpr bool ATC = (OP == kWgrad);
-  static constexpr bool BTC = (OP != kFwd);
+  // wgrad reads the packed transposed copies, so only dgrad has a strided operand
+  static constexpr bool ATC = false;
+  static constexpr bool BTC = (OP == kDgrad);
   uint32_t off_a[4], off_b[4];
   int w, wi, wj, lane;
 
@@ -638,16 +680,19 @@ struct Pipe {
 //     run; wait for stage kt+1 and pass one barrier; read the first half of
 //     stage kt+1's fragments while the MFMAs of stage kt's second half run.
 // One barrier per stage, and no MFMA waits on an LDS read.
-template <int OP>
+// OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or fp32
+// accumulate for wgrad).  Units of split wgrad experts store fp32 partials.
+template <int OP, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
-  constexpr bool ATC = (OP == kWgrad);
-  constexpr bool BTC = (OP != kFwd);
+  constexpr bool ATC = Pipe<OP>::ATC;
+  constexpr bool BTC = Pipe<OP>::BTC;
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
+  __shared__ int s_pprefix[kMaxGroups + 1];
   __shared__ int s_scratch[4];
 
-  GroupTable tb{s_end, s_uprefix, s_sprefix, s_scratch};
+  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
   const int total = build_group_table<OP>(p, tb);
   const UnitShape us = unit_shape<OP>(p);
 
@@ -661,8 +706,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   pipe.wi = pipe.w >> 1;
   pipe.wj = pipe.w & 1;
   // DMA offsets depend only on the operands' row strides (fixed per launch).
-  dma_offsets<ATC>(pipe.off_a, (OP == kFwd ? p.k : p.n) * 2, pipe.w, pipe.lane);
-  dma_offsets<BTC>(pipe.off_b, p.k * 2, pipe.w, pipe.lane);
+  const int lda = OP == kFwd ? p.k * 2 : OP == kDgrad ? p.n * 2 : (int)(p.ldp * 2);
+  const int ldb = OP == kWgrad ? (int)(p.ldp * 2) : p.k * 2;
+  dma_offsets<ATC>(pipe.off_a, lda, pipe.w, pipe.lane);
+  dma_offsets<BTC>(pipe.off_b, ldb, pipe.w, pipe.lane);
 
   Unit cur = decode_unit<OP>(p, tb, us, total, vb);
   if (cur.valid) pipe.prefetch(cur);
@@ -691,7 +738,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     __syncthreads();  // every wave is done reading LDS before the next unit's loads
     const Unit nxt = decode_unit<OP>(p, tb, us, total, u + P);
     if (nxt.valid) pipe.prefetch(nxt);
-    store_tile(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane, cur.mode);
+    if (OUT == kStoreF32 || cur.mode == OUT)
+      store_tile<OUT>(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane);
+    else
+      store_tile<kStoreF32>(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane);
     cur = nxt;
   }
   wait_vm_lgkm<0>();
@@ -707,10 +757,11 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(GemmParams p) {
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
+  __shared__ int s_pprefix[kMaxGroups + 1];
   __shared__ int s_scratch[4];
   __shared__ int s_pick[2];
 
-  GroupTable tb{s_end, s_uprefix, s_sprefix, s_scratch};
+  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
   build_group_table<kWgrad>(p, tb);
   const int E = p.num_groups;
   const int t = threadIdx.x;
@@ -774,14 +825,87 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(GemmParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// wgrad: packed transposed copies of G and X
+// ---------------------------------------------------------------------------
+// dst[c][P_e + r] = src[s_e + r][c] for the m_e rows of group e and zero up to
+// m_e rounded up to kGroupPad, where P_e is the exclusive prefix of the padded
+// sizes.  With the reduction (rows) contiguous and every group's rows starting
+// on a 64-byte boundary, the wgrad tiles read both operands exactly like fwd
+// reads X and W.  Persistent grid over 64 x 64 tiles, transposed through LDS;
+// bound by HBM bandwidth (each element read once and written once).
+__global__ __launch_bounds__(kThreads) void wgrad_pack_kernel(PackParams q) {
+  __shared__ int s_end[kMaxGroups];
+  __shared__ int s_uprefix[kMaxGroups + 1];
+  __shared__ int s_sprefix[kMaxGroups];
+  __shared__ int s_pprefix[kMaxGroups + 1];
+  __shared__ int s_scratch[4];
+  __shared__ __attribute__((aligned(16))) uint16_t s_tile[64][72];
+
+  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
+  build_group_table<kWgrad>(q.g, tb);
+  const int E = q.g.num_groups;
+  const int total = s_pprefix[E];
+  const int tiles_c = q.cols / 64;
+  const int tiles = (total + 63) / 64 * tiles_c;
+  const int t = threadIdx.x;
+  for (int u = blockIdx.x; u < tiles; u += gridDim.x) {
+    const int pt = u / tiles_c, ct = u - pt * tiles_c;
+    {  // gather: thread t reads 16 columns of packed row pt*64 + t/4
+      const int pr = t >> 2, c0 = (t & 3) * 16;
+      const int P = pt * 64 + pr;
+      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+      if (P < total) {
+        int lo = 0, hi = E - 1;  // smallest e with pprefix[e + 1] > P
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_pprefix[mid + 1] > P) hi = mid; else lo = mid + 1;
+        }
+        const int gs = lo == 0 ? 0 : s_end[lo - 1];
+        const int r = P - s_pprefix[lo];
+        if (r < s_end[lo] - gs) {
+          const uint16_t* sp = q.src + (int64_t)(gs + r) * q.cols + ct * 64 + c0;
+          v0 = *reinterpret_cast<const u32x4*>(sp);
+          v1 = *reinterpret_cast<const u32x4*>(sp + 8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s_tile[c0 + i][pr] = (uint16_t)(v0[i >> 1] >> ((i & 1) * 16));
+        s_tile[c0 + 8 + i][pr] = (uint16_t)(v1[i >> 1] >> ((i & 1) * 16));
+      }
+    }
+    __syncthreads();
+    {  // scatter: thread t writes 16 packed rows of column ct*64 + t/4
+      const int c = t >> 2, p0 = (t & 3) * 16;
+      uint16_t* dp = q.dst + (int64_t)(ct * 64 + c) * q.g.ldp + pt * 64 + p0;
+      *reinterpret_cast<u32x4*>(dp) = *reinterpret_cast<const u32x4*>(&s_tile[c][p0]);
+      *reinterpret_cast<u32x4*>(dp + 8) = *reinterpret_cast<const u32x4*>(&s_tile[c][p0 + 8]);
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
+
+hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(wgrad_pack_kernel, dim3(grid), dim3(kThreads), 0, stream, q);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(kThreads);
   switch (op) {
-    case kFwd: hipLaunchKernelGGL(grouped_gemm_kernel<kFwd>, g, blk, 0, stream, p); break;
-    case kDgrad: hipLaunchKernelGGL(grouped_gemm_kernel<kDgrad>, g, blk, 0, stream, p); break;
-    case kWgrad: hipLaunchKernelGGL(grouped_gemm_kernel<kWgrad>, g, blk, 0, stream, p); break;
+    case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16>), g, blk, 0, stream, p); break;
+    case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16>), g, blk, 0, stream, p); break;
+    case kWgrad:
+      if (!p.out_fp32)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16>), g, blk, 0, stream, p);
+      else if (!p.accumulate)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32>), g, blk, 0, stream, p);
+      else
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc>), g, blk, 0, stream, p);
+      break;
   }
   return hipGetLastError();
 }

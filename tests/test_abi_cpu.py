@@ -127,7 +127,15 @@ def test_chunk_rows_rule(lib):
 def test_workspace_covers_every_grouping(lib, M, N, K, E):
     """The workspace bound holds for any split of M rows into E groups."""
     R = lib.grouped_det_gemm_wgrad_chunk_rows(M, N, K, E)
-    have = lib.grouped_det_gemm_wgrad_workspace_bytes(M, N, K, E) - 4096
+    # partial-tile slots the library provisions: floor(M/R) + #experts with > R rows
+    big = min(E, M // (R + 1))
+    slots_cap = 0 if big == 0 else M // R + big
+    # workspace = 4 KiB head + partial tiles + packed G^T [N, ldp] and X^T [K, ldp]
+    # (bf16, every group padded to 32 rows)
+    ldp = -(-(M + 31 * E) // 64) * 64
+    assert lib.grouped_det_gemm_wgrad_workspace_bytes(M, N, K, E) >= \
+        4096 + slots_cap * N * K * 4 + 2 * (N + K) * ldp
+    have = slots_cap * N * K * 4
     rng = np.random.default_rng(M + E)
     cases = [np.full(E, M // E) for _ in range(1)]
     cases.append(np.array([M] + [0] * (E - 1)))
