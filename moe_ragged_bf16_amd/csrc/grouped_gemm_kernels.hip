@@ -470,8 +470,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out,
         }
       }
   } else {
-    // chunk c = (ib, jb pair): 2 column blocks x 4 steps = 8 loads of 16 bytes
-    f32x4 cur[8], nxt[8];
+    // chunk c = (ib, jb pair): 2 column blocks x 4 steps = 8 loads of 16 bytes;
+    // 4 chunks (32 loads, half the tile) are in flight at any time.
+    constexpr int kAhead = 4;
+    f32x4 buf[kAhead][8];
     auto load_chunk = [&](f32x4 (&dst)[8], int c) {
       const int ib = c >> 1, jb0 = (c & 1) * 2;
 #pragma unroll
@@ -481,10 +483,10 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out,
         for (int g = 0; g < 4; ++g) dst[h * 4 + g] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, g * 32, 0);
       }
     };
-    load_chunk(cur, 0);
+#pragma unroll
+    for (int c = 0; c < kAhead; ++c) load_chunk(buf[c], c);
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (c + 1 < 8) load_chunk(nxt, c + 1);
       const int ib = c >> 1, jb0 = (c & 1) * 2;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -492,7 +494,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out,
         const f32x16& a = acc[ib][jb0 + h];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          f32x4 v = cur[h * 4 + g];
+          f32x4 v = buf[c % kAhead][h * 4 + g];
           v[0] = __fadd_rn(v[0], a[4 * g + 0]);
           v[1] = __fadd_rn(v[1], a[4 * g + 1]);
           v[2] = __fadd_rn(v[2], a[4 * g + 2]);
@@ -500,8 +502,7 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out,
           __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, g * 32, 0);
         }
       }
-#pragma unroll
-      for (int q = 0; q < 8; ++q) cur[q] = nxt[q];
+      if (c + kAhead < 8) load_chunk(buf[c % kAhead], c + kAhead);
     }
   }
 }
