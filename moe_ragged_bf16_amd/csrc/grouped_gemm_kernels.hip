@@ -321,6 +321,21 @@ __device__ __forceinline__ void wait_vm_lgkm() {
   __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
 }
 
+// Waits until at most `n` vector memory operations of this wave are
+// outstanding (and all its LDS reads have returned).  The immediate is the
+// largest available one not above n, so the wait is never shorter than asked.
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 63) wait_vm_lgkm<63>();
+  else if (n >= 56) wait_vm_lgkm<56>();
+  else if (n >= 48) wait_vm_lgkm<48>();
+  else if (n >= 40) wait_vm_lgkm<40>();
+  else if (n >= 32) wait_vm_lgkm<32>();
+  else if (n >= 24) wait_vm_lgkm<24>();
+  else if (n >= 16) wait_vm_lgkm<16>();
+  else if (n >= 8) wait_vm_lgkm<8>();
+  else wait_vm_lgkm<0>();
+}
+
 // Workgroup barrier for the stage ring.  __syncthreads() would also make the
 // compiler drain every outstanding load (its workgroup fence waits for all
 // vector memory operations), which would serialise the LDS-DMA prefetch; the
@@ -419,90 +434,96 @@ enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2 };
 // is dropped.  Masked lanes use it, so every wave issues the same instructions.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-// Writes this wave's accumulators to the tile at `out` (row stride ldc
-// elements): rows i < i_valid and columns j < j_valid of the 256 x 256 tile
-// (j_valid is a multiple of 64, so a 32-column block is valid or not as a
-// whole).  All accesses are buffer operations on one descriptor covering the
-// tile's valid extent; masked lanes get an offset the range check turns away.
-// The fused accumulate reads the destination in chunks of 8 x 16 bytes per lane,
-// one chunk ahead of the chunk being added and stored (one IEEE fp32 add per
-// element, no contraction).
+// The output tile of one unit as seen by one wave: rows i < i_valid and
+// columns j < j_valid of the 256 x 256 tile at `out` (row stride ldc elements;
+// j_valid is a multiple of 64, so a 32-column block is valid or not as a whole).
+// All accesses are buffer operations on one descriptor covering the tile's
+// valid extent; masked lanes get an offset the range check turns away, so a
+// wave always issues the same memory instructions: 32 per row half (rows
+// 0..63 or 64..127 of the wave's sub-tile) for a store, 32 + 32 for an
+// accumulate.
+struct OutTile {
+  __amdgpu_buffer_rsrc_t rs;
+  int base;       // this lane's byte offset of (row 0, column block 0)
+  int ldc_b, esz;
+  int row0;       // wi * 128 + lane % 32
+  int i_valid, j_valid, wj;
+};
+
+__device__ __forceinline__ OutTile out_tile(void* out, int64_t ldc, int i_valid, int j_valid, int wi, int wj,
+                                            int lane, int esz) {
+  OutTile t;
+  t.ldc_b = (int)ldc * esz;
+  t.esz = esz;
+  const int extent = i_valid > 0 ? (i_valid - 1) * t.ldc_b + j_valid * esz : 0;
+  t.rs = __builtin_amdgcn_make_buffer_rsrc(out, 0, extent, 0x00020000);
+  t.row0 = wi * 128 + (lane & 31);
+  t.base = t.row0 * t.ldc_b + (wj * 128 + (lane >> 5) * 4) * esz;
+  t.i_valid = i_valid;
+  t.j_valid = j_valid;
+  t.wj = wj;
+  return t;
+}
+
+// Offset of row block ib, column block jb (the 8-column step is an immediate).
+__device__ __forceinline__ uint32_t tile_off(const OutTile& t, int ib, int jb) {
+  const bool ok = (t.row0 + ib * 32) < t.i_valid && (t.wj * 128 + jb * 32) < t.j_valid;
+  return ok ? (uint32_t)(t.base + ib * 32 * t.ldc_b + jb * 32 * t.esz) : kOutOfRange;
+}
+
+// Stores row blocks ib0, ib0+1 (bf16: 8 bytes per lane and step; fp32: 16).
 template <int mode>
-__device__ __forceinline__ void store_tile(const f32x16 (&acc)[4][4], void* out, int64_t ldc, int i_valid,
-                                           int j_valid, int wi, int wj, int lane) {
-  const int lr = lane & 31, lh = (lane >> 5) * 4;
-  const int esz = mode == kStoreBf16 ? 2 : 4;
-  const int ldc_b = (int)ldc * esz;
-  const int extent = i_valid > 0 ? (i_valid - 1) * ldc_b + j_valid * esz : 0;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(out, 0, extent, 0x00020000);
-  const int base = (wi * 128 + lr) * ldc_b + (wj * 128 + lh) * esz;
-  // offset of row block ib, column block jb (the 8-column step g is added as an immediate)
-  auto voff = [&](int ib, int jb) -> uint32_t {
-    const bool ok = (wi * 128 + ib * 32 + lr) < i_valid && (wj * 128 + jb * 32) < j_valid;
-    return ok ? (uint32_t)(base + ib * 32 * ldc_b + jb * 32 * esz) : kOutOfRange;
-  };
-  if constexpr (mode == kStoreBf16) {
+__device__ __forceinline__ void store_half(const f32x16 (&acc)[4][4], const OutTile& t, int ib0) {
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+  for (int ib = ib0; ib < ib0 + 2; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const uint32_t o = voff(ib, jb);
-        const f32x16& a = acc[ib][jb];
+    for (int jb = 0; jb < 4; ++jb) {
+      const uint32_t o = tile_off(t, ib, jb);
+      const f32x16& a = acc[ib][jb];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+      for (int g = 0; g < 4; ++g) {
+        if constexpr (mode == kStoreBf16) {
           u32x2 pk;
           pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
           pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, o, g * 16, 0);
-        }
-      }
-  } else if constexpr (mode == kStoreF32) {
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const uint32_t o = voff(ib, jb);
-        const f32x16& a = acc[ib][jb];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
+          __builtin_amdgcn_raw_buffer_store_b64(pk, t.rs, o, g * 16, 0);
+        } else {
           const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, g * 32, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, t.rs, o, g * 32, 0);
         }
       }
-  } else {
-    // chunk c = (ib, jb pair): 2 column blocks x 4 steps = 8 loads of 16 bytes;
-    // 4 chunks (32 loads, half the tile) are in flight at any time.
-    constexpr int kAhead = 4;
-    f32x4 buf[kAhead][8];
-    auto load_chunk = [&](f32x4 (&dst)[8], int c) {
-      const int ib = c >> 1, jb0 = (c & 1) * 2;
+    }
+}
+
+// Reads chunk c (row block c/2, column blocks 2(c%2), 2(c%2)+1) of the fp32
+// destination: 8 loads of 16 bytes per lane.
+__device__ __forceinline__ void load_chunk(f32x4 (&dst)[8], const OutTile& t, int c) {
+  const int ib = c >> 1, jb0 = (c & 1) * 2;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t o = voff(ib, jb0 + h);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t o = tile_off(t, ib, jb0 + h);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) dst[h * 4 + g] = __builtin_amdgcn_raw_buffer_load_b128(rs, o, g * 32, 0);
-      }
-    };
+    for (int g = 0; g < 4; ++g) dst[h * 4 + g] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, o, g * 32, 0);
+  }
+}
+
+// dst = RN32(dst + acc) for chunk c, from its values `old` read earlier: one
+// IEEE fp32 add per element of the finished product (no contraction).
+__device__ __forceinline__ void add_store_chunk(const f32x16 (&acc)[4][4], const f32x4 (&old)[8],
+                                                const OutTile& t, int c) {
+  const int ib = c >> 1, jb0 = (c & 1) * 2;
 #pragma unroll
-    for (int c = 0; c < kAhead; ++c) load_chunk(buf[c], c);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t o = tile_off(t, ib, jb0 + h);
+    const f32x16& a = acc[ib][jb0 + h];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int ib = c >> 1, jb0 = (c & 1) * 2;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t o = voff(ib, jb0 + h);
-        const f32x16& a = acc[ib][jb0 + h];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 v = buf[c % kAhead][h * 4 + g];
-          v[0] = __fadd_rn(v[0], a[4 * g + 0]);
-          v[1] = __fadd_rn(v[1], a[4 * g + 1]);
-          v[2] = __fadd_rn(v[2], a[4 * g + 2]);
-          v[3] = __fadd_rn(v[3], a[4 * g + 3]);
-          __builtin_amdgcn_raw_buffer_store_b128(v, rs, o, g * 32, 0);
-        }
-      }
-      if (c + kAhead < 8) load_chunk(buf[c % kAhead], c + kAhead);
+    for (int g = 0; g < 4; ++g) {
+      f32x4 v = old[h * 4 + g];
+      v[0] = __fadd_rn(v[0], a[4 * g + 0]);
+      v[1] = __fadd_rn(v[1], a[4 * g + 1]);
+      v[2] = __fadd_rn(v[2], a[4 * g + 2]);
+      v[3] = __fadd_rn(v[3], a[4 * g + 3]);
+      __builtin_amdgcn_raw_buffer_store_b128(v, t.rs, o, g * 32, 0);
     }
   }
 }
@@ -647,12 +668,19 @@ struct Pipe {
   // half are in (fa0, fb0).  Issues stage kt+3 (zeros past the last stage),
   // runs the first half's MFMAs while reading the second half, waits for stage
   // kt+1 and passes the barrier, then runs the second half's MFMAs while
-  // reading stage kt+1's first half.  Branch-free: every step issues the same
-  // loads, so the wait counts are constants and the step is one scheduling
-  // region in which the loads, LDS reads and MFMAs interleave.
+  // reading stage kt+1's first half.  Apart from the optional reads below, the
+  // step is branch-free: one scheduling region in which the loads, LDS reads
+  // and MFMAs interleave.
+  //
+  // The wait for stage kt+1 must allow exactly the memory operations issued
+  // after its loads: the 16 loads of stages kt+2 and kt+3 plus the extra
+  // operations issued after those stages' loads (the previous unit's last
+  // stores), which the caller tracks in e2 (two steps back) and e1 (one step
+  // back).
   template <int S>
   __device__ __forceinline__ void step(f32x16 (&acc)[4][4], bf16x8 (&fa0)[4], bf16x8 (&fb0)[4],
-                                       bf16x8 (&fa1)[4], bf16x8 (&fb1)[4], const Unit& x, int kt) const {
+                                       bf16x8 (&fa1)[4], bf16x8 (&fb1)[4], const Unit& x, int kt, int& e1,
+                                       int& e2) const {
     constexpr int S1 = (S + 1) & 3, S3 = (S + 3) & 3;
     constexpr int kReads = 4 * (ATC ? 2 : 1) + 4 * (BTC ? 2 : 1);
     load_frags<ATC, BTC>(fa1, fb1, stage_a<S>(), stage_b<S>(), wi, wj, 1, lane);
@@ -666,8 +694,10 @@ struct Pipe {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
-    wait_vm_lgkm<2 * kDmaPerStage>();  // stage kt+1 has landed (kt+2, kt+3 may be in flight)
-    lds_barrier();                      // ... in every wave; stage kt's reads all returned
+    wait_vm(2 * kDmaPerStage + e2 + e1);  // stage kt+1 has landed
+    e2 = e1;
+    e1 = 0;
+    lds_barrier();  // ... in every wave; stage kt's reads all returned
     // (after the last stage these reads are discarded)
     mma_16_with_reads<ATC, BTC>(acc, fa1, fb1, fa0, fb0, stage_a<S1>(), stage_b<S1>(), wi, wj, 0, lane);
   }
@@ -714,6 +744,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
   Unit cur = decode_unit<OP>(p, tb, us, total, vb);
   if (cur.valid) pipe.prefetch(cur);
+  int tail = 0;  // memory operations issued after the current unit's prefetch
   for (int u = vb; cur.valid; u += P) {
     f32x16 acc[4][4];
 #pragma unroll
@@ -723,26 +754,48 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int x = 0; x < 16; ++x) acc[ib][jb][x] = 0.0f;
 
+    const bool rmw = OUT == kStoreF32Acc && cur.mode == kStoreF32Acc;
     if (cur.nk > 0) {
       bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-      wait_vm_lgkm<2 * kDmaPerStage>();
-      lds_barrier();  // stage 0 visible
+      int e1 = tail, e2 = 0;
+      wait_vm(2 * kDmaPerStage + tail);  // stage 0 has landed
+      lds_barrier();                     // ... in every wave
       load_frags<ATC, BTC>(fa0, fb0, stage_a<0>(), stage_b<0>(), pipe.wi, pipe.wj, 0, pipe.lane);
       for (int kt = 0; kt < cur.nk; kt += 4) {
-        pipe.template step<0>(acc, fa0, fb0, fa1, fb1, cur, kt);
-        pipe.template step<1>(acc, fa0, fb0, fa1, fb1, cur, kt + 1);
-        pipe.template step<2>(acc, fa0, fb0, fa1, fb1, cur, kt + 2);
-        pipe.template step<3>(acc, fa0, fb0, fa1, fb1, cur, kt + 3);
+        pipe.template step<0>(acc, fa0, fb0, fa1, fb1, cur, kt, e1, e2);
+        pipe.template step<1>(acc, fa0, fb0, fa1, fb1, cur, kt + 1, e1, e2);
+        pipe.template step<2>(acc, fa0, fb0, fa1, fb1, cur, kt + 2, e1, e2);
+        pipe.template step<3>(acc, fa0, fb0, fa1, fb1, cur, kt + 3, e1, e2);
       }
     }
     wait_vm_lgkm<0>();
     __syncthreads();  // every wave is done reading LDS before the next unit's loads
+
+    // Epilogue, overlapped with the next unit's first stages: the first row
+    // half is written before the next unit's prefetch, the second half after
+    // it (32 operations that the next unit's stage waits allow for).
     const Unit nxt = decode_unit<OP>(p, tb, us, total, u + P);
-    if (nxt.valid) pipe.prefetch(nxt);
-    if (OUT == kStoreF32 || cur.mode == OUT)
-      store_tile<OUT>(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane);
-    else
-      store_tile<kStoreF32>(acc, cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane);
+    const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane,
+                                cur.mode == kStoreBf16 ? 2 : 4);
+    if (rmw) {
+      f32x4 old[4][8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) load_chunk(old[c], ot, c);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) add_store_chunk(acc, old[c], ot, c);
+#pragma unroll
+      for (int c = 4; c < 8; ++c) load_chunk(old[c - 4], ot, c);
+      if (nxt.valid) pipe.prefetch(nxt);
+#pragma unroll
+      for (int c = 4; c < 8; ++c) add_store_chunk(acc, old[c - 4], ot, c);
+    } else {
+      if (OUT == kStoreF32 || cur.mode == OUT) store_half<OUT == kStoreF32Acc ? kStoreF32 : OUT>(acc, ot, 0);
+      else store_half<kStoreF32>(acc, ot, 0);
+      if (nxt.valid) pipe.prefetch(nxt);
+      if (OUT == kStoreF32 || cur.mode == OUT) store_half<OUT == kStoreF32Acc ? kStoreF32 : OUT>(acc, ot, 2);
+      else store_half<kStoreF32>(acc, ot, 2);
+    }
+    tail = 32;
     cur = nxt;
   }
   wait_vm_lgkm<0>();
