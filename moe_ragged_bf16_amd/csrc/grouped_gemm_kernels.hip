@@ -330,10 +330,12 @@ __device__ __forceinline__ void wait_vm_lgkm() {
 __device__ __forceinline__ void wait_vm(int n) {
   if (n >= 63) wait_vm_lgkm<63>();
   else if (n >= 56) wait_vm_lgkm<56>();
+  else if (n >= 52) wait_vm_lgkm<52>();
   else if (n >= 48) wait_vm_lgkm<48>();
   else if (n >= 40) wait_vm_lgkm<40>();
   else if (n >= 32) wait_vm_lgkm<32>();
   else if (n >= 24) wait_vm_lgkm<24>();
+  else if (n >= 20) wait_vm_lgkm<20>();
   else if (n >= 16) wait_vm_lgkm<16>();
   else if (n >= 8) wait_vm_lgkm<8>();
   else wait_vm_lgkm<0>();
@@ -383,14 +385,16 @@ __device__ __forceinline__ bf16x8 load_frag(const uint8_t* st, int row0, int kk,
   }
 }
 
+// Reads in the order the MFMAs of the next half step consume them (mma_16 runs
+// row block ib outermost: its first 4 MFMAs need all of fb and fa[0], then one
+// more fa every 4 MFMAs), so each read has at least 8 MFMAs of latency cover.
 template <bool ATC, bool BTC>
 __device__ __forceinline__ void load_frags(bf16x8 (&fa)[4], bf16x8 (&fb)[4], const uint8_t* sa, const uint8_t* sb,
                                            int wi, int wj, int kk, int lane) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    fa[b] = load_frag<ATC>(sa, wi * 128 + b * 32, kk, lane);
-    fb[b] = load_frag<BTC>(sb, wj * 128 + b * 32, kk, lane);
-  }
+  for (int b = 0; b < 4; ++b) fb[b] = load_frag<BTC>(sb, wj * 128 + b * 32, kk, lane);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) fa[b] = load_frag<ATC>(sa, wi * 128 + b * 32, kk, lane);
 }
 
 // Wave w owns the 128 x 128 sub-tile (i: 128*(w/2), j: 128*(w%2)) as 4 x 4
@@ -404,23 +408,18 @@ __device__ __forceinline__ void mma_16(f32x16 (&acc)[4][4], const bf16x8 (&fa)[4
       acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[jb], fa[ib], acc[ib][jb], 0, 0, 0);
 }
 
-// 16 MFMAs on (fa0, fb0) while the LDS reads into (fa1, fb1) of step `kk` are
-// interleaved between them (scheduling groups pin the order).
-template <bool ATC, bool BTC>
-__device__ __forceinline__ void mma_16_with_reads(f32x16 (&acc)[4][4], const bf16x8 (&fa0)[4],
-                                                  const bf16x8 (&fb0)[4], bf16x8 (&fa1)[4], bf16x8 (&fb1)[4],
-                                                  const uint8_t* sa, const uint8_t* sb, int wi, int wj, int kk,
-                                                  int lane) {
-  constexpr int kReads = 4 * (ATC ? 2 : 1) + 4 * (BTC ? 2 : 1);
-  constexpr int kPer = 16 / kReads;
-  load_frags<ATC, BTC>(fa1, fb1, sa, sb, wi, wj, kk, lane);
-  mma_16(acc, fa0, fb0);
-#pragma unroll
-  for (int r = 0; r < kReads; ++r) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+// Scheduling groups that pin the order of one half step: 16 MFMAs with `R` LDS
+// reads and `V` DMA loads spread evenly between them.
+template <int R, int V, int m = 0>
+__device__ __forceinline__ void interleave_16() {
+  if constexpr (m < 16) {
+    constexpr int d = (m + 1) * R / 16 - m * R / 16;
+    constexpr int v = (m + 1) * V / 16 - m * V / 16;
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    interleave_16<R, V, m + 1>();
   }
-  if (16 - kPer * kReads > 0) __builtin_amdgcn_sched_group_barrier(0x008, 16 - kPer * kReads, 0);
 }
 
 // fp32 -> bf16 with round to nearest, ties to even (NaN stays NaN).
@@ -439,94 +438,166 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // The output tile of one unit as seen by one wave: rows i < i_valid and
 // columns j < j_valid of the 256 x 256 tile at `out` (row stride ldc elements;
-// j_valid is a multiple of 64, so a 32-column block is valid or not as a whole).
-// All accesses are buffer operations on one descriptor covering the tile's
-// valid extent; masked lanes get an offset the range check turns away, so a
-// wave always issues the same memory instructions: 32 per row half (rows
-// 0..63 or 64..127 of the wave's sub-tile) for a store, 32 + 32 for an
-// accumulate.
+// j_valid is a multiple of 64).  The epilogue passes the accumulators through
+// LDS (a "staging" buffer of 8 KiB per wave) so that every global access covers
+// whole 256-byte row segments: one load or store instruction moves 4 rows x 256
+// bytes, 16 bytes per lane, where the MFMA layout itself (lane = row) would give
+// 32 rows x 16 bytes.  All global accesses are buffer operations on one
+// descriptor covering the tile's valid extent; masked lanes get an offset the
+// range check turns away, so a wave always issues the same instructions.
 struct OutTile {
   __amdgpu_buffer_rsrc_t rs;
-  int base;       // this lane's byte offset of (row 0, column block 0)
-  int ldc_b, esz;
-  int row0;       // wi * 128 + lane % 32
-  int i_valid, j_valid, wj;
+  int ldc_b;
+  int rows_left;   // i_valid minus this lane's first row (wi * 128 + lane / 16)
+  uint32_t base0;  // byte offset of this lane's 16 bytes in its first row (kOutOfRange if the columns are invalid)
+  uint32_t base1;  // the same 64 columns further (fp32 second half)
 };
+
+// Keeps a per-lane value opaque to the compiler at this point, so that the
+// addresses derived from it are formed where they are used instead of being
+// hoisted out of the unit loop (where they would only occupy registers).
+__device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ OutTile out_tile(void* out, int64_t ldc, int i_valid, int j_valid, int wi, int wj,
                                             int lane, int esz) {
   OutTile t;
   t.ldc_b = (int)ldc * esz;
-  t.esz = esz;
   const int extent = i_valid > 0 ? (i_valid - 1) * t.ldc_b + j_valid * esz : 0;
   t.rs = __builtin_amdgcn_make_buffer_rsrc(out, 0, extent, 0x00020000);
-  t.row0 = wi * 128 + (lane & 31);
-  t.base = t.row0 * t.ldc_b + (wj * 128 + (lane >> 5) * 4) * esz;
-  t.i_valid = i_valid;
-  t.j_valid = j_valid;
-  t.wj = wj;
+  const int row0 = wi * 128 + (lane >> 4);
+  const int col0 = wj * 128 + (lane & 15) * (16 / esz);
+  const uint32_t b = (uint32_t)(row0 * t.ldc_b + col0 * esz);
+  t.base0 = col0 < j_valid ? b : kOutOfRange;
+  t.base1 = col0 + 64 < j_valid ? b + 256 : kOutOfRange;
+  t.rows_left = i_valid - row0;
+  opaque(t.base0);
+  opaque(t.base1);
+  opaque(t.rows_left);
   return t;
 }
 
-// Offset of row block ib, column block jb (the 8-column step is an immediate).
-__device__ __forceinline__ uint32_t tile_off(const OutTile& t, int ib, int jb) {
-  const bool ok = (t.row0 + ib * 32) < t.i_valid && (t.wj * 128 + jb * 32) < t.j_valid;
-  return ok ? (uint32_t)(t.base + ib * 32 * t.ldc_b + jb * 32 * t.esz) : kOutOfRange;
+// Global byte offset of read q (rows 4q .. 4q+3) of row slab ib, column half jh
+// (fp32 only: the wave's second 64 columns).  An invalid base stays out of
+// range after the row step (kOutOfRange + less than 2^31).
+__device__ __forceinline__ uint32_t slab_off(const OutTile& t, int ib, int q, int jh) {
+  const int r = ib * 32 + q * 4;
+  const uint32_t b = jh ? t.base1 : t.base0;
+  return r < t.rows_left ? b + (uint32_t)(r * t.ldc_b) : kOutOfRange;
 }
 
-// Stores row blocks ib0, ib0+1 (bf16: 8 bytes per lane and step; fp32: 16).
+// Staging layout: 32 rows of 256 bytes; 16-byte chunk c of row r at chunk
+// c ^ (r % 16), so that both the writes (lane = row) and the reads (16 lanes per
+// row) spread over all banks.
+struct Staging {
+  uint8_t* w;  // this lane's write row: xb + (lane % 32) * 256 (+ 8 for the upper half-wave's bf16 pair)
+  uint8_t* r;  // this lane's first read row: xb + (lane / 16) * 256
+  int sw;      // lane % 16: the write rows' swizzle (row % 16), and the read chunk
+};
+
+__device__ __forceinline__ Staging staging(uint8_t* xb, int lane, int half_b) {
+  Staging x;
+  int wo = (lane & 31) * 256 + (lane >> 5) * half_b;
+  int ro = (lane >> 4) * 256;
+  opaque(wo);
+  opaque(ro);
+  x.w = xb + wo;
+  x.r = xb + ro;
+  x.sw = lane & 15;
+  return x;
+}
+
+// Writes row slab ib (rows 32 ib .. 32 ib + 31 of the wave's sub-tile) to the
+// staging buffer: bf16, all 128 columns; fp32, the 64 columns of half jh.
 template <int mode>
-__device__ __forceinline__ void store_half(const f32x16 (&acc)[4][4], const OutTile& t, int ib0) {
+__device__ __forceinline__ void stage_slab(const f32x16 (&acc)[4][4], const Staging& x, int ib, int jh, int lane) {
+  if constexpr (mode == kStoreBf16) {
 #pragma unroll
-  for (int ib = ib0; ib < ib0 + 2; ++ib)
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const uint32_t o = tile_off(t, ib, jb);
-      const f32x16& a = acc[ib][jb];
+    for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        if constexpr (mode == kStoreBf16) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
-          pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, t.rs, o, g * 16, 0);
-        } else {
-          const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(v, t.rs, o, g * 32, 0);
-        }
+        const f32x16& a = acc[ib][jb];
+        u32x2 pk;
+        pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
+        pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+        *reinterpret_cast<u32x2*>(x.w + (((jb * 4 + g) ^ x.sw) << 4)) = pk;
       }
-    }
-}
-
-// Reads chunk c (row block c/2, column blocks 2(c%2), 2(c%2)+1) of the fp32
-// destination: 8 loads of 16 bytes per lane.
-__device__ __forceinline__ void load_chunk(f32x4 (&dst)[8], const OutTile& t, int c) {
-  const int ib = c >> 1, jb0 = (c & 1) * 2;
+  } else {
+    const int h = lane >> 5;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t o = tile_off(t, ib, jb0 + h);
+    for (int jl = 0; jl < 2; ++jl)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) dst[h * 4 + g] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, o, g * 32, 0);
+      for (int g = 0; g < 4; ++g) {
+        const f32x16& a = acc[ib][jh * 2 + jl];
+        const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        *reinterpret_cast<f32x4*>(x.w + (((jl * 8 + g * 2 + h) ^ x.sw) << 4)) = v;
+      }
   }
 }
 
-// dst = RN32(dst + acc) for chunk c, from its values `old` read earlier: one
-// IEEE fp32 add per element of the finished product (no contraction).
-__device__ __forceinline__ void add_store_chunk(const f32x16 (&acc)[4][4], const f32x4 (&old)[8],
-                                                const OutTile& t, int c) {
-  const int ib = c >> 1, jb0 = (c & 1) * 2;
+// Reads the staged slab back row-major: read q gives this lane 16 bytes of row
+// 4q + lane/16 (whose swizzle is (4q + lane/16) % 16).
+__device__ __forceinline__ void unstage_slab(u32x4 (&v)[8], const Staging& x, int lane) {
+  const int rl = lane >> 4;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t o = tile_off(t, ib, jb0 + h);
-    const f32x16& a = acc[ib][jb0 + h];
+  for (int q = 0; q < 8; ++q)
+    v[q] = *reinterpret_cast<const u32x4*>(x.r + q * 1024 + ((x.sw ^ ((4 * q + rl) & 15)) << 4));
+}
+
+// Vector memory operations one wave issues in the epilogue of each mode.
+template <int mode>
+constexpr int epilogue_ops() {
+  return mode == kStoreBf16 ? 32 : mode == kStoreF32 ? 64 : 128;
+}
+
+// Stores the wave's sub-tile (bf16 or fp32).
+template <int mode>
+__device__ __forceinline__ void epilogue_store(const f32x16 (&acc)[4][4], const OutTile& t, uint8_t* xb, int lane) {
+  constexpr int kHalves = mode == kStoreBf16 ? 1 : 2;
+  const Staging x = staging(xb, lane, mode == kStoreBf16 ? 8 : 0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 v = old[h * 4 + g];
-      v[0] = __fadd_rn(v[0], a[4 * g + 0]);
-      v[1] = __fadd_rn(v[1], a[4 * g + 1]);
-      v[2] = __fadd_rn(v[2], a[4 * g + 2]);
-      v[3] = __fadd_rn(v[3], a[4 * g + 3]);
-      __builtin_amdgcn_raw_buffer_store_b128(v, t.rs, o, g * 32, 0);
+  for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+    for (int jh = 0; jh < kHalves; ++jh) {
+      __builtin_amdgcn_sched_barrier(0);  // one slab at a time (bounds the registers in use)
+      stage_slab<mode>(acc, x, ib, jh, lane);
+      u32x4 v[8];
+      unstage_slab(v, x, lane);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) __builtin_amdgcn_raw_buffer_store_b128(v[q], t.rs, slab_off(t, ib, q, jh), 0, 0);
+    }
+}
+
+// dst = RN32(dst + acc) over the wave's fp32 sub-tile: one IEEE fp32 add per
+// element of the finished product (no contraction).  The destination reads of
+// the next half slab are in flight while the current one is staged and added.
+__device__ __forceinline__ void epilogue_accumulate(const f32x16 (&acc)[4][4], const OutTile& t, uint8_t* xb,
+                                                    int lane) {
+  const Staging x = staging(xb, lane, 0);
+  f32x4 old[2][8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, 0);
+#pragma unroll
+  for (int hs = 0; hs < 8; ++hs) {
+    const int ib = hs >> 1, jh = hs & 1;
+    __builtin_amdgcn_sched_barrier(0);  // one half slab at a time (bounds the registers in use)
+    if (hs + 1 < 8) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        old[(hs + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, (hs + 1) >> 1, q, (hs + 1) & 1), 0, 0);
+    }
+    stage_slab<kStoreF32>(acc, x, ib, jh, lane);
+    u32x4 v[8];
+    unstage_slab(v, x, lane);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const f32x4 n = __builtin_bit_cast(f32x4, v[q]);
+      f32x4 o = old[hs & 1][q];
+      o[0] = __fadd_rn(o[0], n[0]);
+      o[1] = __fadd_rn(o[1], n[1]);
+      o[2] = __fadd_rn(o[2], n[2]);
+      o[3] = __fadd_rn(o[3], n[3]);
+      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, jh), 0, 0);
     }
   }
 }
@@ -653,66 +724,74 @@ struct Pipe {
   uint32_t off_a[4], off_b[4];
   int w, wi, wj, lane;
 
+  // This wave's 4 DMA loads of operand A (resp. B) of stage kt into buffer S.
   template <int S>
-  __device__ __forceinline__ void issue(const Unit& x, int kt) const {
-    const bool live = kt < x.nk;
-    dma_stage<ATC>(x.a, off_a, stage_a<S>() + w * 1024, kt, live);
-    dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, live);
+  __device__ __forceinline__ void issue_a(const Unit& x, int kt) const {
+    dma_stage<ATC>(x.a, off_a, stage_a<S>() + w * 1024, kt, kt < x.nk);
+  }
+  template <int S>
+  __device__ __forceinline__ void issue_b(const Unit& x, int kt) const {
+    dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, kt < x.nk);
   }
 
-  // Stages 0..2 of a unit, into buffers 0..2.
+  // Stages 0..2 of a unit into buffers 0..2, and operand A of stage 3.
   __device__ __forceinline__ void prefetch(const Unit& x) const {
-    issue<0>(x, 0);
-    issue<1>(x, 1);
-    issue<2>(x, 2);
+    issue_a<0>(x, 0);
+    issue_b<0>(x, 0);
+    issue_a<1>(x, 1);
+    issue_b<1>(x, 1);
+    issue_a<2>(x, 2);
+    issue_b<2>(x, 2);
+    issue_a<3>(x, 3);
   }
 
   // Stage kt, held in buffer S = kt % 4.  On entry the fragments of its first
-  // half are in (fa0, fb0).  Issues stage kt+3 (zeros past the last stage),
-  // runs the first half's MFMAs while reading the second half, waits for stage
-  // kt+1 and passes the barrier, then runs the second half's MFMAs while
-  // reading stage kt+1's first half.  Apart from the optional reads below, the
-  // step is branch-free: one scheduling region in which the loads, LDS reads
-  // and MFMAs interleave.
+  // half are in (fa0, fb0) and operand A of stage kt+3 is loading.  First
+  // half: issue operand B of stage kt+3 (zeros past the last stage) and run the
+  // first half's MFMAs while reading the second half's fragments; then wait for
+  // stage kt+1 and pass the barrier, after which no wave reads buffer S any
+  // more.  Second half: issue operand A of stage kt+4 into buffer S and run the
+  // second half's MFMAs while reading stage kt+1's first half.  Each half thus
+  // spreads 4 loads per wave over its 16 MFMAs (the address unit never sees
+  // all of a stage's loads at once), and the step is branch-free: one
+  // scheduling region per half in which loads, LDS reads and MFMAs interleave.
   //
   // The wait for stage kt+1 must allow exactly the memory operations issued
-  // after its loads: the 16 loads of stages kt+2 and kt+3 plus the extra
-  // operations issued after those stages' loads (the previous unit's last
-  // stores), which the caller tracks in e2 (two steps back) and e1 (one step
-  // back).
+  // after its last loads (operand B, one step before stage kt's): the 16 loads
+  // of stage kt+2 and stage kt+3 plus the extra operations issued after those
+  // (the previous unit's last stores), which the caller tracks in e2 (two steps
+  // back) and e1 (one step back).
   template <int S>
   __device__ __forceinline__ void step(f32x16 (&acc)[4][4], bf16x8 (&fa0)[4], bf16x8 (&fb0)[4],
                                        bf16x8 (&fa1)[4], bf16x8 (&fb1)[4], const Unit& x, int kt, int& e1,
                                        int& e2) const {
     constexpr int S1 = (S + 1) & 3, S3 = (S + 3) & 3;
+    static_assert(kDmaPerStage == 8, "4 loads per operand and wave");
     constexpr int kReads = 4 * (ATC ? 2 : 1) + 4 * (BTC ? 2 : 1);
     load_frags<ATC, BTC>(fa1, fb1, stage_a<S>(), stage_b<S>(), wi, wj, 1, lane);
-    issue<S3>(x, kt + 3);
+    issue_b<S3>(x, kt + 3);
     mma_16(acc, fa0, fb0);
-    // interleave: 16 MFMAs with the reads of the second half and the 8 loads
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, kReads / 8, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
+    interleave_16<kReads, kDmaPerStage / 2>();
     wait_vm(2 * kDmaPerStage + e2 + e1);  // stage kt+1 has landed
     e2 = e1;
     e1 = 0;
     lds_barrier();  // ... in every wave; stage kt's reads all returned
     // (after the last stage these reads are discarded)
-    mma_16_with_reads<ATC, BTC>(acc, fa1, fb1, fa0, fb0, stage_a<S1>(), stage_b<S1>(), wi, wj, 0, lane);
+    load_frags<ATC, BTC>(fa0, fb0, stage_a<S1>(), stage_b<S1>(), wi, wj, 0, lane);
+    issue_a<S>(x, kt + 4);
+    mma_16(acc, fa1, fb1);
+    interleave_16<kReads, kDmaPerStage / 2>();
   }
 };
 
 // Per unit, with stages of 32 reductions in a ring of 4 LDS buffers:
-//   * stages 0..2 are loaded ahead (for every unit but the first, during the
-//     previous unit's epilogue);
-//   * stage kt: issue stage kt+3 into the buffer stage kt-1 used; read the
-//     second half of stage kt's fragments while the MFMAs of its first half
-//     run; wait for stage kt+1 and pass one barrier; read the first half of
-//     stage kt+1's fragments while the MFMAs of stage kt's second half run.
+//   * stages 0..2 and operand A of stage 3 are loaded ahead (for every unit
+//     but the first, during the previous unit's epilogue);
+//   * stage kt: issue operand B of stage kt+3 into the buffer stage kt-1 used;
+//     read the second half of stage kt's fragments while the MFMAs of its
+//     first half run; wait for stage kt+1 and pass one barrier; issue operand
+//     A of stage kt+4 into stage kt's buffer and read the first half of stage
+//     kt+1's fragments while the MFMAs of stage kt's second half run.
 // One barrier per stage, and no MFMA waits on an LDS read.
 // OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or fp32
 // accumulate for wgrad).  Units of split wgrad experts store fp32 partials.
@@ -747,7 +826,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 
   Unit cur = decode_unit<OP>(p, tb, us, total, vb);
   if (cur.valid) pipe.prefetch(cur);
-  int tail = 0;  // memory operations issued after the current unit's prefetch
+  int tail = 0;  // memory operations issued between stage 2 and stage 3's operand A of the current unit
   for (int u = vb; cur.valid; u += P) {
     f32x16 acc[4][4];
 #pragma unroll
@@ -761,7 +840,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     if (cur.nk > 0) {
       bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
       int e1 = tail, e2 = 0;
-      wait_vm(2 * kDmaPerStage + tail);  // stage 0 has landed
+      wait_vm(2 * kDmaPerStage + kDmaPerStage / 2 + tail);  // stage 0 has landed
       lds_barrier();                     // ... in every wave
       load_frags<ATC, BTC>(fa0, fb0, stage_a<0>(), stage_b<0>(), pipe.wi, pipe.wj, 0, pipe.lane);
       for (int kt = 0; kt < cur.nk; kt += 4) {
@@ -774,31 +853,38 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     wait_vm_lgkm<0>();
     __syncthreads();  // every wave is done reading LDS before the next unit's loads
 
-    // Epilogue, overlapped with the next unit's first stages: the first row
-    // half is written before the next unit's prefetch, the second half after
-    // it (32 operations that the next unit's stage waits allow for).
+    // Epilogue, overlapped with the next unit's first stages: stages 0..2 load
+    // into their buffers while the results pass through the staging buffers
+    // (the last stage buffers, 8 KiB per wave) to memory; operand A of stage 3
+    // follows once every wave is done with them.
     const Unit nxt = decode_unit<OP>(p, tb, us, total, u + P);
+    if (nxt.valid) {
+      pipe.template issue_a<0>(nxt, 0);
+      pipe.template issue_b<0>(nxt, 0);
+      pipe.template issue_a<1>(nxt, 1);
+      pipe.template issue_b<1>(nxt, 1);
+      pipe.template issue_a<2>(nxt, 2);
+      pipe.template issue_b<2>(nxt, 2);
+    }
+    uint8_t* xb = (pipe.w < 2 ? s_a3 : s_b3) + (pipe.w & 1) * 8192;
     const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane,
                                 cur.mode == kStoreBf16 ? 2 : 4);
-    if (rmw) {
-      f32x4 old[4][8];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) load_chunk(old[c], ot, c);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) add_store_chunk(acc, old[c], ot, c);
-#pragma unroll
-      for (int c = 4; c < 8; ++c) load_chunk(old[c - 4], ot, c);
-      if (nxt.valid) pipe.prefetch(nxt);
-#pragma unroll
-      for (int c = 4; c < 8; ++c) add_store_chunk(acc, old[c - 4], ot, c);
+    if constexpr (OP != kWgrad) {
+      epilogue_store<kStoreBf16>(acc, ot, xb, pipe.lane);
+      tail = epilogue_ops<kStoreBf16>();
+    } else if (rmw) {
+      epilogue_accumulate(acc, ot, xb, pipe.lane);
+      tail = epilogue_ops<kStoreF32Acc>();
+    } else if (OUT == kStoreBf16 && cur.mode == kStoreBf16) {
+      epilogue_store<kStoreBf16>(acc, ot, xb, pipe.lane);
+      tail = epilogue_ops<kStoreBf16>();
     } else {
-      if (OUT == kStoreF32 || cur.mode == OUT) store_half<OUT == kStoreF32Acc ? kStoreF32 : OUT>(acc, ot, 0);
-      else store_half<kStoreF32>(acc, ot, 0);
-      if (nxt.valid) pipe.prefetch(nxt);
-      if (OUT == kStoreF32 || cur.mode == OUT) store_half<OUT == kStoreF32Acc ? kStoreF32 : OUT>(acc, ot, 2);
-      else store_half<kStoreF32>(acc, ot, 2);
+      epilogue_store<kStoreF32>(acc, ot, xb, pipe.lane);
+      tail = epilogue_ops<kStoreF32>();
     }
-    tail = 32;
+    wait_vm_lgkm<63>();  // the staging reads have returned ...
+    lds_barrier();       // ... in every wave
+    if (nxt.valid) pipe.template issue_a<3>(nxt, 3);
     cur = nxt;
   }
   wait_vm_lgkm<0>();
