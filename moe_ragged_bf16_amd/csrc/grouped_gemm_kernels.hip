@@ -507,6 +507,17 @@ __device__ __forceinline__ Staging staging(uint8_t* xb, int lane, int half_b) {
   return x;
 }
 
+// Reads one accumulator out of its AGPR where the epilogue uses it.  Left to
+// itself the compiler copies the whole 256-register tile into VGPRs when the
+// main loop ends, which leaves no room for anything else and makes it spill.
+// (The epilogue starts long after the last MFMA: a wait for all memory
+// operations and a workgroup barrier lie between them.)
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 // Writes row slab ib (rows 32 ib .. 32 ib + 31 of the wave's sub-tile) to the
 // staging buffer: bf16, all 128 columns; fp32, the 64 columns of half jh.
 template <int mode>
@@ -518,8 +529,8 @@ __device__ __forceinline__ void stage_slab(const f32x16 (&acc)[4][4], const Stag
       for (int g = 0; g < 4; ++g) {
         const f32x16& a = acc[ib][jb];
         u32x2 pk;
-        pk[0] = pack_bf16x2(a[4 * g + 0], a[4 * g + 1]);
-        pk[1] = pack_bf16x2(a[4 * g + 2], a[4 * g + 3]);
+        pk[0] = pack_bf16x2(acc_read(a[4 * g + 0]), acc_read(a[4 * g + 1]));
+        pk[1] = pack_bf16x2(acc_read(a[4 * g + 2]), acc_read(a[4 * g + 3]));
         *reinterpret_cast<u32x2*>(x.w + (((jb * 4 + g) ^ x.sw) << 4)) = pk;
       }
   } else {
@@ -529,7 +540,8 @@ __device__ __forceinline__ void stage_slab(const f32x16 (&acc)[4][4], const Stag
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16& a = acc[ib][jh * 2 + jl];
-        const f32x4 v = {a[4 * g + 0], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+        const f32x4 v = {acc_read(a[4 * g + 0]), acc_read(a[4 * g + 1]), acc_read(a[4 * g + 2]),
+                         acc_read(a[4 * g + 3])};
         *reinterpret_cast<f32x4*>(x.w + (((jl * 8 + g * 2 + h) ^ x.sw) << 4)) = v;
       }
   }
