@@ -309,6 +309,10 @@ __device__ __forceinline__ void dma_stage(const Operand& o, const uint32_t (&off
     bytes = rows > 0 ? (rows - 1) * o.ld_bytes + o.aux : 0;
   }
   if (!live) bytes = 0;  // a stage past the unit's last one: the loads only write zeros
+  // The size is uniform but may be computed with vector instructions (there is
+  // no scalar med3); reading it back as a scalar keeps the descriptor in SGPRs
+  // instead of making the compiler wrap every load in a readfirstlane loop.
+  bytes = uniform(bytes);
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, 0x00020000);
 #pragma unroll
@@ -818,7 +822,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   __shared__ int s_scratch[4];
 
   GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
-  const int total = build_group_table<OP>(p, tb);
+  const int total = uniform(build_group_table<OP>(p, tb));  // (from LDS: make it visibly uniform)
   const UnitShape us = unit_shape<OP>(p);
 
   const int P = gridDim.x;
