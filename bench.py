@@ -163,15 +163,17 @@ def main():
     y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(mdg.wgrad_workspace_bytes(M, N, K, E), 256), dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(mdg.fwd_workspace_bytes(M, N, K, E), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(mdg.dgrad_workspace_bytes(M, N, K, E), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mdg.grouped_det_gemm_fwd(x, w, offs, out=y)
+        mdg.grouped_det_gemm_fwd(x, w, offs, out=y, workspace=ws_f)
         if ev is not None:
             ev[1].record()
-        mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx)
+        mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx, workspace=ws_d)
         if ev is not None:
             ev[2].record()
         mdg.grouped_det_gemm_wgrad(g, x, offs, out=mg, accumulate=True, workspace=ws)
@@ -206,8 +208,8 @@ def main():
     # bitwise rerun check of the measured kernels (outputs must not change)
     y_ref = y.clone()
     dx_ref = dx.clone()
-    mdg.grouped_det_gemm_fwd(x, w, offs, out=y)
-    mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx)
+    mdg.grouped_det_gemm_fwd(x, w, offs, out=y, workspace=ws_f)
+    mdg.grouped_det_gemm_dgrad(g, w, offs, out=dx, workspace=ws_d)
     torch.cuda.synchronize()
     rerun_ok = bool(torch.equal(y.view(torch.int16), y_ref.view(torch.int16)) and
                     torch.equal(dx.view(torch.int16), dx_ref.view(torch.int16)))

@@ -58,14 +58,14 @@
 extern "C" {
 #endif
 
-#define MDG_ABI_VERSION 1
+#define MDG_ABI_VERSION 2
 
 typedef enum {
   MDG_OK = 0,
   MDG_EINVAL = 1,        /* null pointer, negative size, misaligned pointer, bad enum */
   MDG_EUNSUPPORTED = 2,  /* shape outside the supported set, or device is not gfx950 */
   MDG_EOVERLAP = 3,      /* an output shares a byte with an input, offs or the workspace */
-  MDG_EWORKSPACE = 4,    /* wgrad workspace missing or smaller than required */
+  MDG_EWORKSPACE = 4,    /* workspace missing or smaller than required */
   MDG_EHIP = 5           /* the HIP runtime reported an error when enqueueing */
 } mdg_status;
 
@@ -78,25 +78,49 @@ int mdg_abi_version(void);
 const char* mdg_status_string(int status);
 
 /*
+ * Bytes of device workspace grouped_det_gemm_fwd (resp. _dgrad) needs for these
+ * sizes: a small plan table plus fp32 partial tiles of the tail split described
+ * below (at most 8 KiB + 64 MiB).  It depends on the sizes only (never on offs or
+ * the device).  Returns 0 for invalid sizes.
+ */
+size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                            int32_t num_groups);
+size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                              int32_t num_groups);
+
+/*
  * fwd: Y[s_e:t_e] = X[s_e:t_e] @ W[e]^T  (API page, operations table, "fwd").
  *   x  [m_rows, k] bf16, read.        w [num_groups, n, k] bf16, read.
  *   offs [num_groups] int32, read.    y [m_rows, n] bf16, written (rows of groups only).
- * m_rows == 0 enqueues nothing.  y must not overlap x, w or offs.
+ *   workspace: device buffer of at least grouped_det_gemm_fwd_workspace_bytes()
+ *      bytes, 256-byte aligned, owned by the caller, contents on entry ignored;
+ *      must not overlap any other argument.  Two calls that share a workspace must
+ *      be ordered on one stream.
+ * Work is scheduled as 256 x 256 output tiles (units).  When the number of units
+ * U leaves a remainder T = U mod 256 that would occupy only part of the GPU in
+ * the last round, each of those last T units is cut into S consecutive ranges
+ * of its reduction (S <= 8, a function of U and the sizes only); each range is
+ * summed in fp32 in the one fixed order and a second kernel adds the S partial
+ * tiles in range order before rounding to bf16.  Every output is therefore
+ * still a fixed function of the inputs: bitwise identical from run to run.
+ * m_rows == 0 enqueues nothing.  y must not overlap x, w, offs or the workspace.
  */
 int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y,
                          int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                         void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dgrad: dX[s_e:t_e] = G[s_e:t_e] @ W[e], W read in place (API page, operations
  * table, "dgrad").
  *   g  [m_rows, n] bf16, read.        w [num_groups, n, k] bf16, read.
  *   offs [num_groups] int32, read.    dx [m_rows, k] bf16, written (rows of groups only).
- * m_rows == 0 enqueues nothing.  dx must not overlap g, w or offs.
+ *   workspace: as for fwd, of at least grouped_det_gemm_dgrad_workspace_bytes()
+ *      bytes; the same tail split applies (the reduction here runs over n).
+ * m_rows == 0 enqueues nothing.  dx must not overlap g, w, offs or the workspace.
  */
 int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
                            int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace grouped_det_gemm_wgrad needs for these sizes: a small

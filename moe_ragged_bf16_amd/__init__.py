@@ -12,6 +12,8 @@ from .ops import (  # noqa: F401
     grouped_det_gemm_fwd,
     grouped_det_gemm_dgrad,
     grouped_det_gemm_wgrad,
+    fwd_workspace_bytes,
+    dgrad_workspace_bytes,
     wgrad_workspace_bytes,
     wgrad_chunk_rows,
 )

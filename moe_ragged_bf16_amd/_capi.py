@@ -19,6 +19,8 @@ EXPORTED = (
     "mdg_status_string",
     "grouped_det_gemm_fwd",
     "grouped_det_gemm_dgrad",
+    "grouped_det_gemm_fwd_workspace_bytes",
+    "grouped_det_gemm_dgrad_workspace_bytes",
     "grouped_det_gemm_wgrad",
     "grouped_det_gemm_wgrad_workspace_bytes",
     "grouped_det_gemm_wgrad_chunk_rows",
@@ -56,7 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         for name in ("grouped_det_gemm_fwd", "grouped_det_gemm_dgrad"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
-            f.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
+            f.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+        for name in ("grouped_det_gemm_fwd_workspace_bytes", "grouped_det_gemm_dgrad_workspace_bytes"):
+            f = getattr(lib, name)
+            f.restype = sz
+            f.argtypes = [i64, i64, i64, i32]
         lib.grouped_det_gemm_wgrad.restype = ctypes.c_int
         lib.grouped_det_gemm_wgrad.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
                                                i64, i64, i64, i32, vp, sz, vp]

@@ -47,6 +47,27 @@ int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_
   return big == 0 ? 0 : m_rows / chunk_rows + big;
 }
 
+// fwd/dgrad: units of the persistent schedule (an upper bound: row tiles of
+// every group, each group's last one possibly partial, times column tiles).
+int64_t fwd_dgrad_units_ub(Op op, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  const int64_t n_j = (op == kFwd) ? n / kTileJ : (k + kTileJ - 1) / kTileJ;
+  const int64_t row_tiles_ub = (m_rows + kTileI - 1) / kTileI + num_groups;
+  return row_tiles_ub * n_j;
+}
+
+// fwd/dgrad: fp32 partial tiles of the tail split.  The tail holds fewer than
+// kBalanceSlots units, each cut into at most kMaxSplit pieces, and the plan
+// never uses more pieces than kBalanceSlots (nor than this bound).
+int64_t tail_slots(int64_t units_ub) {
+  const int64_t s = units_ub * kMaxSplit;
+  return s < kBalanceSlots ? s : kBalanceSlots;
+}
+
+size_t fwd_dgrad_workspace(Op op, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  const int64_t slots = tail_slots(fwd_dgrad_units_ub(op, m_rows, n, k, num_groups));
+  return (size_t)kTailHeadBytes + (size_t)slots * kTileI * kTileJ * sizeof(float);
+}
+
 // Row length of the packed transposed copies: every group padded to kGroupPad
 // rows (sum of padded sizes <= M + (kGroupPad - 1) * E), rounded up to 64.
 int64_t wgrad_packed_ld(int64_t m_rows, int32_t num_groups) {
@@ -138,19 +159,25 @@ int persistent_grid(int64_t units_upper_bound, int cus) {
 }
 
 int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
-                 int64_t n, int64_t k, int32_t num_groups, void* stream) {
+                 int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   int st = check_sizes(m_rows, n, k, num_groups);
   if (st != MDG_OK) return st;
   // Row-indexed tensors may be NULL when there are no rows (never dereferenced).
   if (!w || !offs || (m_rows > 0 && (!a || !out))) return MDG_EINVAL;
   if (!aligned16(a) || !aligned16(w) || !aligned4(offs) || !aligned16(out)) return MDG_EINVAL;
+  const size_t need = fwd_dgrad_workspace(op, m_rows, n, k, num_groups);
+  if (!workspace || workspace_bytes < need) return MDG_EWORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MDG_EINVAL;
   const int64_t a_cols = (op == kFwd) ? k : n;
   const int64_t o_cols = (op == kFwd) ? n : k;
   const Range ra = range_of(a, m_rows * a_cols * 2);
   const Range rw = range_of(w, (int64_t)num_groups * n * k * 2);
   const Range ro = range_of(offs, (int64_t)num_groups * 4);
   const Range ry = range_of(out, m_rows * o_cols * 2);
-  if (overlaps(ry, ra) || overlaps(ry, rw) || overlaps(ry, ro)) return MDG_EOVERLAP;
+  const Range rws = range_of(workspace, (int64_t)need);
+  if (overlaps(ry, ra) || overlaps(ry, rw) || overlaps(ry, ro) || overlaps(ry, rws)) return MDG_EOVERLAP;
+  if (overlaps(rws, ra) || overlaps(rws, rw) || overlaps(rws, ro)) return MDG_EOVERLAP;
   if (m_rows == 0) return MDG_OK;
 
   DeviceInfo dev;
@@ -167,10 +194,22 @@ int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void*
   p.n = (int32_t)n;
   p.k = (int32_t)k;
   p.num_groups = num_groups;
-  const int64_t n_j = (op == kFwd) ? n / kTileJ : (k + kTileJ - 1) / kTileJ;
-  const int64_t row_tiles_ub = (m_rows + kTileI - 1) / kTileI + num_groups;
-  const int grid = persistent_grid(row_tiles_ub * n_j, dev.cus);
-  if (launch_gemm(op, p, grid, static_cast<hipStream_t>(stream)) != hipSuccess) return MDG_EHIP;
+  const int64_t units_ub = fwd_dgrad_units_ub(op, m_rows, n, k, num_groups);
+  const int64_t slots = tail_slots(units_ub);
+  char* ws = static_cast<char*>(workspace);
+  p.tail_head = reinterpret_cast<int32_t*>(ws);
+  p.partial = reinterpret_cast<float*>(ws + kTailHeadBytes);
+  p.tail_slots = (int32_t)slots;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int grid = persistent_grid(units_ub + slots, dev.cus);
+  if (launch_gemm(op, p, grid, s) != hipSuccess) return MDG_EHIP;
+  // Split tail units (at most kBalanceSlots / 2 of them, as each has >= 2
+  // pieces): the reduce kernel reads the plan the GEMM kernel wrote and exits
+  // at once when there is none.
+  if (slots >= 2) {
+    const int64_t gy = std::min<int64_t>(kBalanceSlots / 2, slots / 2);
+    if (launch_tail_reduce(p, 8, (int)gy, s) != hipSuccess) return MDG_EHIP;
+  }
   return MDG_OK;
 }
 
@@ -189,20 +228,32 @@ const char* mdg_status_string(int s) {
     case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
     case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 256 == 0, k % 64 == 0, 1 <= groups <= 1024)";
     case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
-    case MDG_EWORKSPACE: return "wgrad workspace missing or too small";
+    case MDG_EWORKSPACE: return "workspace missing or too small";
     case MDG_EHIP: return "HIP runtime error";
     default: return "unknown status";
   }
 }
 
+size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return fwd_dgrad_workspace(kFwd, m_rows, n, k, num_groups);
+}
+
+size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return fwd_dgrad_workspace(kDgrad, m_rows, n, k, num_groups);
+}
+
 int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
-                         int64_t n, int64_t k, int32_t num_groups, void* stream) {
-  return fwd_or_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, stream);
+                         int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  return fwd_or_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, stream);
 }
 
 int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
-                           int64_t n, int64_t k, int32_t num_groups, void* stream) {
-  return fwd_or_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, stream);
+                           int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return fwd_or_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes, stream);
 }
 
 int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {

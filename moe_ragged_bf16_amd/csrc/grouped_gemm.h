@@ -19,6 +19,11 @@ constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
 constexpr int kGroupPad = 32;    // wgrad: each group's rows are zero-padded to a multiple of this
 constexpr int64_t kMaxRows = 4000000;  // m_rows limit (keeps the packed layout's buffer ranges < 2^31)
+// fwd/dgrad tail split: the units left over after whole rounds of kBalanceSlots
+// units are cut into up to kMaxSplit consecutive reduction ranges (see the kernels).
+constexpr int kBalanceSlots = 256;
+constexpr int kMaxSplit = 8;
+constexpr int kTailHeadBytes = 8192;  // plan + per-tail-unit descriptors, at the workspace head
 
 enum Op : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
@@ -27,7 +32,7 @@ struct GemmParams {
   const uint16_t* b;      // fwd: W, dgrad: W, wgrad: X
   const int32_t* offs;    // [E] cumulative end offsets (device)
   void* out;              // fwd: Y, dgrad: dX, wgrad: dW
-  float* partial;         // wgrad: fp32 partial tiles of split groups
+  float* partial;         // fp32 partial tiles: wgrad, of split groups; fwd/dgrad, of split tail units
   int64_t m_rows;
   int32_t n, k, num_groups;
   int32_t chunk_rows;     // wgrad rows per chunk
@@ -36,7 +41,17 @@ struct GemmParams {
   const uint16_t* gt;     // wgrad: G^T [n, ldp], groups zero-padded to kGroupPad rows (workspace)
   const uint16_t* xt;     // wgrad: X^T [k, ldp], same layout (workspace)
   int64_t ldp;            // wgrad: row length of gt / xt (elements)
+  int32_t tail_slots;     // fwd/dgrad: partial tiles the workspace holds (0: no tail split)
+  int32_t* tail_head;     // fwd/dgrad: kTailHeadBytes of workspace: the tail plan for the reduce kernel
 };
+
+// One entry of the fwd/dgrad tail table (written by the GEMM kernel, read by
+// the tail reduce kernel): where a split tail unit's output tile goes.
+struct TailUnit {
+  uint16_t* out;
+  int32_t ldc, i_valid, j_valid, pad;
+};
+static_assert(sizeof(TailUnit) == 24, "tail table entry");
 
 // wgrad pack: dst[c][P_e + r] = src[s_e + r][c] for r < m_e, 0 up to the padded
 // group end (P_e = sum of the padded sizes of the groups before e).
@@ -51,6 +66,7 @@ struct PackParams {
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream);
+hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 
 // Host-side sizing helpers (capi.cpp).
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);

@@ -461,6 +461,15 @@ struct OutTile {
 // addresses derived from it are formed where they are used instead of being
 // hoisted out of the unit loop (where they would only occupy registers).
 __device__ __forceinline__ void opaque(int& v) { asm volatile("" : "+v"(v)); }
+
+// This lane's index, computed where it is used (a volatile statement the
+// compiler cannot hoist): the epilogue's lane-dependent addresses are then
+// formed in the epilogue rather than kept in registers across the main loop.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 __device__ __forceinline__ void opaque(uint32_t& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ OutTile out_tile(void* out, int64_t ldc, int i_valid, int j_valid, int wi, int wj,
@@ -497,6 +506,7 @@ struct Staging {
   uint8_t* w;  // this lane's write row: xb + (lane % 32) * 256 (+ 8 for the upper half-wave's bf16 pair)
   uint8_t* r;  // this lane's first read row: xb + (lane / 16) * 256
   int sw;      // lane % 16: the write rows' swizzle (row % 16), and the read chunk
+  int rl;      // lane / 16: the read row within each group of 4
 };
 
 __device__ __forceinline__ Staging staging(uint8_t* xb, int lane, int half_b) {
@@ -505,9 +515,13 @@ __device__ __forceinline__ Staging staging(uint8_t* xb, int lane, int half_b) {
   int ro = (lane >> 4) * 256;
   opaque(wo);
   opaque(ro);
+  int sw = lane & 15, rl = lane >> 4;
+  opaque(sw);
+  opaque(rl);
   x.w = xb + wo;
   x.r = xb + ro;
-  x.sw = lane & 15;
+  x.sw = sw;
+  x.rl = rl;
   return x;
 }
 
@@ -553,11 +567,10 @@ __device__ __forceinline__ void stage_slab(const f32x16 (&acc)[4][4], const Stag
 
 // Reads the staged slab back row-major: read q gives this lane 16 bytes of row
 // 4q + lane/16 (whose swizzle is (4q + lane/16) % 16).
-__device__ __forceinline__ void unstage_slab(u32x4 (&v)[8], const Staging& x, int lane) {
-  const int rl = lane >> 4;
+__device__ __forceinline__ void unstage_slab(u32x4 (&v)[8], const Staging& x) {
 #pragma unroll
   for (int q = 0; q < 8; ++q)
-    v[q] = *reinterpret_cast<const u32x4*>(x.r + q * 1024 + ((x.sw ^ ((4 * q + rl) & 15)) << 4));
+    v[q] = *reinterpret_cast<const u32x4*>(x.r + q * 1024 + ((x.sw ^ ((4 * q + x.rl) & 15)) << 4));
 }
 
 // Vector memory operations one wave issues in the epilogue of each mode.
@@ -578,7 +591,7 @@ __device__ __forceinline__ void epilogue_store(const f32x16 (&acc)[4][4], const 
       __builtin_amdgcn_sched_barrier(0);  // one slab at a time (bounds the registers in use)
       stage_slab<mode>(acc, x, ib, jh, lane);
       u32x4 v[8];
-      unstage_slab(v, x, lane);
+      unstage_slab(v, x);
 #pragma unroll
       for (int q = 0; q < 8; ++q) __builtin_amdgcn_raw_buffer_store_b128(v[q], t.rs, slab_off(t, ib, q, jh), 0, 0);
     }
@@ -604,7 +617,7 @@ __device__ __forceinline__ void epilogue_accumulate(const f32x16 (&acc)[4][4], c
     }
     stage_slab<kStoreF32>(acc, x, ib, jh, lane);
     u32x4 v[8];
-    unstage_slab(v, x, lane);
+    unstage_slab(v, x);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const f32x4 n = __builtin_bit_cast(f32x4, v[q]);
@@ -698,6 +711,90 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
       x.mode = kStoreBf16;
     }
   }
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// fwd/dgrad tail split
+// ---------------------------------------------------------------------------
+// With U units on a persistent grid, the U mod kBalanceSlots units left after
+// whole rounds would run on a few CUs while the rest idle.  Those T tail units
+// are instead cut into S consecutive ranges of their reduction (whole groups
+// of 4 stages, S = min(kBalanceSlots / T, kMaxSplit, groups, slots / T)); each
+// piece writes a dense fp32 partial tile and a second kernel adds the S
+// partials in range order.  The plan is a function of the sizes and offs only.
+// Each piece still sums its range in the one fixed order, so results stay
+// bitwise reproducible.
+struct Plan {
+  int full;   // units processed whole (the first `full` work items)
+  int tail;   // split tail units (0: no split)
+  int split;  // pieces per tail unit
+  int items;  // full + tail * split
+};
+
+template <int OP>
+__device__ __forceinline__ Plan make_plan(const GemmParams& p, int total) {
+  Plan pl{total, 0, 1, total};
+  if (OP == kWgrad || p.tail_slots < 2) return pl;
+  const int t = total % kBalanceSlots;
+  if (t == 0) return pl;
+  const int groups = ((OP == kFwd ? p.k : p.n) / kTileR + 3) / 4;
+  const int sp = min(min(kBalanceSlots / t, kMaxSplit), min(groups, p.tail_slots / t));
+  if (sp < 2) return pl;
+  pl.full = total - t;
+  pl.tail = t;
+  pl.split = sp;
+  pl.items = pl.full + t * sp;
+  return pl;
+}
+
+// Moves an operand's start k0 reductions further (the buffer ranges keep
+// ending where the operand's valid data ends).
+__device__ __forceinline__ void shift_rc(Operand& o, int k0) {
+  o.base += 2 * k0;
+  o.lim -= 2 * k0;
+  o.aux -= 2 * k0;
+}
+__device__ __forceinline__ void shift_tc(Operand& o, int k0) {
+  o.base += (int64_t)k0 * o.ld_bytes;
+  o.lim -= k0;
+}
+
+__device__ __forceinline__ TailUnit* tail_table(const GemmParams& p) {
+  return reinterpret_cast<TailUnit*>(reinterpret_cast<uint8_t*>(p.tail_head) + 256);
+}
+
+// Work item v: a whole unit, or piece s of tail unit t.
+template <int OP>
+__device__ __forceinline__ Unit decode_item(const GemmParams& p, const GroupTable& tb, const UnitShape& us,
+                                            int total, const Plan& pl, int v) {
+  if (OP == kWgrad || v < pl.full) return decode_unit<OP>(p, tb, us, total, v);
+  Unit x;
+  x.valid = v < pl.items;
+  if (!x.valid) return x;
+  const int q = v - pl.full;
+  const int t = q / pl.split, sp = q - t * pl.split;
+  x = decode_unit<OP>(p, tb, us, total, pl.full + t);
+  if (sp == 0 && threadIdx.x == 0) {  // where the reduce kernel writes this tile
+    TailUnit* tu = tail_table(p) + t;
+    tu->out = static_cast<uint16_t*>(x.out);
+    tu->ldc = (int)x.ldc;
+    tu->i_valid = x.i_valid;
+    tu->j_valid = x.j_valid;
+    tu->pad = 0;
+  }
+  const int g = x.nk / 4;
+  const int g0 = sp * g / pl.split, g1 = (sp + 1) * g / pl.split;
+  const int k0 = 4 * g0 * kTileR;
+  x.nk = 4 * (g1 - g0);
+  shift_rc(x.a, k0);
+  if (OP == kFwd) shift_rc(x.b, k0);
+  else shift_tc(x.b, k0);
+  x.out = p.partial + (int64_t)q * (kTileI * kTileJ);  // slot t * split + sp
+  x.ldc = kTileJ;
+  x.i_valid = kTileI;
+  x.j_valid = kTileJ;
+  x.mode = kStoreF32;
   return x;
 }
 
@@ -800,6 +897,32 @@ struct Pipe {
   }
 };
 
+// The epilogue of one unit in its store mode; returns the number of vector
+// memory operations it issued.
+template <int OP, int OUT>
+__device__ __forceinline__ int run_epilogue(const f32x16 (&acc)[4][4], const Unit& cur, const OutTile& ot,
+                                            uint8_t* xb, int lane, bool rmw) {
+  if constexpr (OP != kWgrad) {
+    if (cur.mode == kStoreBf16) {
+      epilogue_store<kStoreBf16>(acc, ot, xb, lane);
+      return epilogue_ops<kStoreBf16>();
+    }
+    epilogue_store<kStoreF32>(acc, ot, xb, lane);  // a piece of a split tail unit: fp32 partial tile
+    return epilogue_ops<kStoreF32>();
+  } else {
+    if (rmw) {
+      epilogue_accumulate(acc, ot, xb, lane);
+      return epilogue_ops<kStoreF32Acc>();
+    }
+    if (OUT == kStoreBf16 && cur.mode == kStoreBf16) {
+      epilogue_store<kStoreBf16>(acc, ot, xb, lane);
+      return epilogue_ops<kStoreBf16>();
+    }
+    epilogue_store<kStoreF32>(acc, ot, xb, lane);
+    return epilogue_ops<kStoreF32>();
+  }
+}
+
 // Per unit, with stages of 32 reductions in a ring of 4 LDS buffers:
 //   * stages 0..2 and operand A of stage 3 are loaded ahead (for every unit
 //     but the first, during the previous unit's epilogue);
@@ -824,6 +947,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
   const int total = uniform(build_group_table<OP>(p, tb));  // (from LDS: make it visibly uniform)
   const UnitShape us = unit_shape<OP>(p);
+  const Plan pl = make_plan<OP>(p, total);
+  if (OP != kWgrad && p.tail_head != nullptr && blockIdx.x == 0 && threadIdx.x == 0) {
+    p.tail_head[0] = pl.tail;  // read by the tail reduce kernel
+    p.tail_head[1] = pl.split;
+  }
 
   const int P = gridDim.x;
   const int bid = blockIdx.x;
@@ -840,7 +968,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   dma_offsets<ATC>(pipe.off_a, lda, pipe.w, pipe.lane);
   dma_offsets<BTC>(pipe.off_b, ldb, pipe.w, pipe.lane);
 
-  Unit cur = decode_unit<OP>(p, tb, us, total, vb);
+  Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
   if (cur.valid) pipe.prefetch(cur);
   int tail = 0;  // memory operations issued between stage 2 and stage 3's operand A of the current unit
   for (int u = vb; cur.valid; u += P) {
@@ -873,7 +1001,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // into their buffers while the results pass through the staging buffers
     // (the last stage buffers, 8 KiB per wave) to memory; operand A of stage 3
     // follows once every wave is done with them.
-    const Unit nxt = decode_unit<OP>(p, tb, us, total, u + P);
+    const Unit nxt = decode_item<OP>(p, tb, us, total, pl, u + P);
     if (nxt.valid) {
       pipe.template issue_a<0>(nxt, 0);
       pipe.template issue_b<0>(nxt, 0);
@@ -882,22 +1010,15 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
       pipe.template issue_a<2>(nxt, 2);
       pipe.template issue_b<2>(nxt, 2);
     }
-    uint8_t* xb = (pipe.w < 2 ? s_a3 : s_b3) + (pipe.w & 1) * 8192;
-    const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, pipe.lane,
+    const int ln = lane_here();
+    const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, ln,
                                 cur.mode == kStoreBf16 ? 2 : 4);
-    if constexpr (OP != kWgrad) {
-      epilogue_store<kStoreBf16>(acc, ot, xb, pipe.lane);
-      tail = epilogue_ops<kStoreBf16>();
-    } else if (rmw) {
-      epilogue_accumulate(acc, ot, xb, pipe.lane);
-      tail = epilogue_ops<kStoreF32Acc>();
-    } else if (OUT == kStoreBf16 && cur.mode == kStoreBf16) {
-      epilogue_store<kStoreBf16>(acc, ot, xb, pipe.lane);
-      tail = epilogue_ops<kStoreBf16>();
-    } else {
-      epilogue_store<kStoreF32>(acc, ot, xb, pipe.lane);
-      tail = epilogue_ops<kStoreF32>();
-    }
+    // Waves 0, 1 stage through s_a3, waves 2, 3 through s_b3.  Each branch names
+    // its array, so the compiler can tell the staging accesses apart from the
+    // stage loads still landing in the other buffers (a pointer selected at run
+    // time would make it wait for all of them first).
+    if (pipe.w < 2) tail = run_epilogue<OP, OUT>(acc, cur, ot, s_a3 + (pipe.w & 1) * 8192, ln, rmw);
+    else tail = run_epilogue<OP, OUT>(acc, cur, ot, s_b3 + (pipe.w & 1) * 8192, ln, rmw);
     wait_vm_lgkm<63>();  // the staging reads have returned ...
     lds_barrier();       // ... in every wave
     if (nxt.valid) pipe.template issue_a<3>(nxt, 3);
@@ -985,6 +1106,45 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// fwd/dgrad: fixed-order sum of the tail pieces
+// ---------------------------------------------------------------------------
+// blockIdx.y picks the tail unit, blockIdx.x a set of rows of its tile.  The
+// plan and the tile destinations come from the workspace head written by the
+// GEMM kernel just before on the same stream.  Each thread adds 8 consecutive
+// columns of one row over the pieces in range order ((p0 + p1) + p2) + ...,
+// rounds to bf16 and writes the valid part of the tile.
+__global__ __launch_bounds__(kThreads) void tail_reduce_kernel(GemmParams p) {
+  const int T = uniform(p.tail_head[0]);
+  const int S = uniform(p.tail_head[1]);
+  const int t = blockIdx.y;
+  if (t >= T || S < 2) return;
+  const TailUnit tu = tail_table(p)[t];
+  const float* part = p.partial + (int64_t)t * S * (kTileI * kTileJ);
+  const int col = (threadIdx.x & 31) * 8;
+  for (int row = blockIdx.x * 8 + (threadIdx.x >> 5); row < kTileI; row += gridDim.x * 8) {
+    const f32x4* src = reinterpret_cast<const f32x4*>(part + row * kTileJ + col);
+    f32x4 lo = src[0], hi = src[1];
+    for (int s = 1; s < S; ++s) {
+      const f32x4* q = reinterpret_cast<const f32x4*>(part + (int64_t)s * (kTileI * kTileJ) + row * kTileJ + col);
+      const f32x4 a = q[0], b = q[1];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lo[c] = __fadd_rn(lo[c], a[c]);
+        hi[c] = __fadd_rn(hi[c], b[c]);
+      }
+    }
+    if (row < tu.i_valid && col < tu.j_valid) {
+      u32x4 pk;
+      pk[0] = pack_bf16x2(lo[0], lo[1]);
+      pk[1] = pack_bf16x2(lo[2], lo[3]);
+      pk[2] = pack_bf16x2(hi[0], hi[1]);
+      pk[3] = pack_bf16x2(hi[2], hi[3]);
+      *reinterpret_cast<u32x4*>(tu.out + (int64_t)row * tu.ldc + col) = pk;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // wgrad: packed transposed copies of G and X
 // ---------------------------------------------------------------------------
 // dst[c][P_e + r] = src[s_e + r][c] for the m_e rows of group e and zero up to
@@ -1066,6 +1226,11 @@ hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream)
         hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc>), g, blk, 0, stream, p);
       break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream) {
+  hipLaunchKernelGGL(tail_reduce_kernel, dim3(grid_x, grid_y), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

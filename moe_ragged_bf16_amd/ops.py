@@ -61,10 +61,31 @@ def _same_device(*ts):
             raise ValueError("all tensors must be on the same device")
 
 
+def fwd_workspace_bytes(m_rows: int, n: int, k: int, num_groups: int) -> int:
+    return int(_capi.load_library().grouped_det_gemm_fwd_workspace_bytes(m_rows, n, k, num_groups))
+
+
+def dgrad_workspace_bytes(m_rows: int, n: int, k: int, num_groups: int) -> int:
+    return int(_capi.load_library().grouped_det_gemm_dgrad_workspace_bytes(m_rows, n, k, num_groups))
+
+
+def _workspace(workspace: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    """The caller's workspace (checked) or a fresh one from torch's allocator."""
+    if workspace is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor")
+    if workspace.numel() < need:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    return workspace
+
+
 def grouped_det_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
-                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Y[s_e:t_e] = X[s_e:t_e] @ W[e]^T, bf16 [M, N].  Rows past offs[E-1] of a
-    freshly allocated Y are left uninitialised."""
+    freshly allocated Y are left uninitialised.  `workspace` (uint8, at least
+    fwd_workspace_bytes()) is allocated per call when not given."""
     _need(x, "x", torch.bfloat16, 2)
     _need(w, "w", torch.bfloat16, 3)
     M, K = x.shape
@@ -78,16 +99,21 @@ def grouped_det_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
         raise ValueError(f"out must have shape {(M, N)}")
     _same_device(x, w, offs, out)
     op = _offs_ptr(offs, E)
+    ws = _workspace(workspace, fwd_workspace_bytes(M, N, K, E), x.device)
+    _same_device(x, ws)
     with torch.cuda.device(x.device):
         st = _capi.load_library().grouped_det_gemm_fwd(
-            x.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E, _stream_handle(x))
+            x.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E,
+            ws.data_ptr(), ws.numel(), _stream_handle(x))
     _capi.check("grouped_det_gemm_fwd", st)
     return out
 
 
 def grouped_det_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
-                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """dX[s_e:t_e] = G[s_e:t_e] @ W[e], bf16 [M, K]."""
+                           out: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dX[s_e:t_e] = G[s_e:t_e] @ W[e], bf16 [M, K].  `workspace` (uint8, at
+    least dgrad_workspace_bytes()) is allocated per call when not given."""
     _need(g, "g", torch.bfloat16, 2)
     _need(w, "w", torch.bfloat16, 3)
     M, N = g.shape
@@ -101,9 +127,12 @@ def grouped_det_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
         raise ValueError(f"out must have shape {(M, K)}")
     _same_device(g, w, offs, out)
     op = _offs_ptr(offs, E)
+    ws = _workspace(workspace, dgrad_workspace_bytes(M, N, K, E), g.device)
+    _same_device(g, ws)
     with torch.cuda.device(g.device):
         st = _capi.load_library().grouped_det_gemm_dgrad(
-            g.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E, _stream_handle(g))
+            g.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E,
+            ws.data_ptr(), ws.numel(), _stream_handle(g))
     _capi.check("grouped_det_gemm_dgrad", st)
     return out
 

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mdg_abi_version() == 1
+    assert lib.mdg_abi_version() == 2
     for s in range(6):
         assert mdg.status_string(s)
     assert mdg.status_string(99) == "unknown status"
@@ -51,33 +51,62 @@ A, B, C, D, WS = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
 @pytest.mark.parametrize("fn", ["grouped_det_gemm_fwd", "grouped_det_gemm_dgrad"])
 def test_fwd_dgrad_refusals(lib, fn):
     f = getattr(lib, fn)
+    wsf = getattr(lib, fn + "_workspace_bytes")
+    need = wsf(8, 256, 256, 4)
+    assert need > 0
+
+    def call(a=A, w=B, o=C, d=D, M=8, N=256, K=256, E=4, ws=WS, wsb=None):
+        return f(a, w, o, d, M, N, K, E, ws, need if wsb is None else wsb, None)
+
     # sizes
-    assert f(A, B, C, D, -1, 256, 256, 4, None) == EINVAL
-    assert f(A, B, C, D, 8, 0, 256, 4, None) == EINVAL
-    assert f(A, B, C, D, 8, 256, 256, 0, None) == EINVAL
-    assert f(A, B, C, D, 8, 128, 256, 4, None) == EUNSUP       # n % 256
-    assert f(A, B, C, D, 8, 256, 96, 4, None) == EUNSUP        # k % 64
-    assert f(A, B, C, D, 8, 256, 256, 1025, None) == EUNSUP    # too many groups
+    assert call(M=-1) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(E=0) == EINVAL
+    assert call(N=128) == EUNSUP       # n % 256
+    assert call(K=96) == EUNSUP        # k % 64
+    assert call(E=1025) == EUNSUP      # too many groups
     # pointers
-    assert f(0, B, C, D, 8, 256, 256, 4, None) == EINVAL
-    assert f(A, 0, C, D, 8, 256, 256, 4, None) == EINVAL
-    assert f(A, B, 0, D, 8, 256, 256, 4, None) == EINVAL
-    assert f(A, B, C, 0, 8, 256, 256, 4, None) == EINVAL
-    assert f(A + 8, B, C, D, 8, 256, 256, 4, None) == EINVAL   # 16-byte alignment
-    assert f(A, B, C + 2, D, 8, 256, 256, 4, None) == EINVAL   # offs needs 4 bytes
-    # overlap of the output with each input
-    assert f(A, B, C, A + 16, 8, 256, 256, 4, None) == EOVERLAP
-    assert f(A, B, C, B + 4096, 8, 256, 256, 4, None) == EOVERLAP
-    assert f(A, B, C, C - 16, 8, 256, 256, 4, None) == EOVERLAP
+    assert call(a=0) == EINVAL
+    assert call(w=0) == EINVAL
+    assert call(o=0) == EINVAL
+    assert call(d=0) == EINVAL
+    assert call(a=A + 8) == EINVAL     # 16-byte alignment
+    assert call(o=C + 2) == EINVAL     # offs needs 4 bytes
+    # workspace
+    assert call(ws=0) == EWS
+    assert call(wsb=need - 1) == EWS
+    assert call(ws=WS + 16) == EINVAL  # 256-byte alignment
+    # overlap of the output with each input and the workspace, of the workspace with the inputs
+    assert call(d=A + 16) == EOVERLAP
+    assert call(d=B + 4096) == EOVERLAP
+    assert call(d=C - 16) == EOVERLAP
+    assert call(ws=D) == EOVERLAP
+    assert call(ws=A) == EOVERLAP
+    assert call(ws=B) == EOVERLAP
     # zero rows: nothing to do, nothing enqueued; row tensors may then be NULL
-    assert f(A, B, C, D, 0, 256, 256, 4, None) == OK
-    assert f(0, B, C, 0, 0, 256, 256, 4, None) == OK
-    assert f(A, B, 0, D, 0, 256, 256, 4, None) == EINVAL      # offs is always needed
+    need0 = wsf(0, 256, 256, 4)
+    assert call(M=0, wsb=need0) == OK
+    assert call(a=0, d=0, M=0, wsb=need0) == OK
+    assert call(o=0, M=0, wsb=need0) == EINVAL      # offs is always needed
 
 
 def test_offs_plus_one_is_accepted_alignment(lib):
     # the m_indptr form passes m_indptr + 1: 4-byte aligned only
-    assert lib.grouped_det_gemm_fwd(A, B, C + 4, D, 0, 256, 256, 4, None) == OK
+    need = lib.grouped_det_gemm_fwd_workspace_bytes(0, 256, 256, 4)
+    assert lib.grouped_det_gemm_fwd(A, B, C + 4, D, 0, 256, 256, 4, WS, need, None) == OK
+
+
+@pytest.mark.parametrize("M,N,K,E", [(512, 256, 256, 4), (16384, 14336, 4096, 8), (0, 256, 64, 1),
+                                     (65536, 2048, 7168, 256), (100, 512, 64, 1000)])
+def test_fwd_dgrad_workspace_rule(lib, M, N, K, E):
+    """8 KiB plan head + fp32 256 x 256 partial tiles for min(256, 8 * units) pieces,
+    units bounded by (row tiles + one partial tile per group) x column tiles."""
+    for fn, cols in (("grouped_det_gemm_fwd_workspace_bytes", N),
+                     ("grouped_det_gemm_dgrad_workspace_bytes", K)):
+        units = (-(-M // 256) + E) * -(-cols // 256)
+        want = 8192 + min(256, 8 * units) * 256 * 256 * 4
+        assert getattr(lib, fn)(M, N, K, E) == want, fn
+        assert getattr(lib, fn)(M, N + 1, K, E) == 0      # invalid sizes
 
 
 def test_wgrad_refusals(lib):
