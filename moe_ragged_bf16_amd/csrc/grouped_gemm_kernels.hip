@@ -8,34 +8,38 @@
 // All three are one tile GEMM  C[i][j] = sum_r A(i, r) * B(j, r):
 //   fwd    i = row, j = n, r = k:   A = X (r contiguous),   B = W[e] (r contiguous)
 //   dgrad  i = row, j = k, r = n:   A = G (r contiguous),   B = W[e] (j contiguous)
-//   wgrad  i = n,   j = k, r = row: A = G (i contiguous),   B = X    (j contiguous)
+//   wgrad  i = n,   j = k, r = row: A = G^T, B = X^T (packed copies, r contiguous)
 //
 // Structure of one launch:
 //  * Offsets are read on the device only.  Each workgroup loads offs into LDS,
 //    clamps them to a non-decreasing sequence in [0, M] (bad offsets stay memory
 //    safe and groups never overlap) and builds, with block-wide scans, the
 //    prefix of work units per group.  No host sync, no atomics.
-//  * Persistent grid: workgroup b walks units v(b), v(b) + P, ... where v
+//  * Persistent grid: workgroup b walks work items v(b), v(b) + P, ... where v
 //    spreads consecutive workgroup ids (dealt round-robin over the 8 XCDs) so
 //    that each XCD works on a contiguous run of units, whose tiles share operand
 //    panels in that XCD's L2.
 //  * Units are 256 x 256 output tiles (fwd/dgrad: one row tile of one group;
-//    wgrad: one row chunk of one expert).  The reduction is staged 64 deep into
-//    double-buffered LDS by buffer loads that write LDS directly (no registers);
-//    the buffer range check turns rows past a group's or chunk's end into zeros.
-//    The next stage's loads are in flight while the MFMAs of the current stage
-//    run; the next unit's first stage loads during the current epilogue.
-//  * LDS layouts follow the memory layout of each operand, with a 16-byte-chunk
-//    XOR swizzle so that both the DMA writes and the fragment reads are free of
-//    bank conflicts:
-//      r-contiguous operand  [256 rows][64 r]  read with ds_read_b128;
-//      i/j-contiguous operand [64 r][256 cols] read with ds_read_b64_tr_b16, the
+//    wgrad: one row chunk of one expert).  fwd/dgrad cut the units left over
+//    after whole rounds into reduction ranges (the tail split below).
+//  * The reduction is staged 32 deep into a ring of 4 LDS buffers per operand
+//    by buffer loads that write LDS directly (no registers); the buffer range
+//    check turns rows past a group's or chunk's end into zeros.  Three stages
+//    are in flight while the MFMAs of the current one run; the next unit's
+//    first stages load during the current epilogue.
+//  * LDS layouts follow the memory layout of each operand, with 16-byte-chunk
+//    XOR swizzles that keep the fragment reads free of bank conflicts:
+//      r-contiguous operand  [256 rows][32 r]  read with ds_read_b128;
+//      i/j-contiguous operand [32 r][256 cols] read with ds_read_b64_tr_b16, the
 //      gfx950 transposing LDS read, which hands each lane 4 consecutive r of one
-//      column, so no operand is ever transposed in registers or in HBM.
-//  * v_mfma_f32_32x32x16_bf16 with fp32 accumulators, one fixed reduction order:
-//    results are bitwise reproducible.
-//  * wgrad row chunks of a split expert write fp32 partials that a second
-//    kernel adds in chunk order (a fixed-order split of the reduction).
+//      column, so no operand is ever transposed in registers.
+//  * v_mfma_f32_16x16x32_bf16 with fp32 accumulators in AGPRs, one fixed
+//    reduction order: results are bitwise reproducible.
+//  * Epilogues pass each wave's results through LDS so that global accesses
+//    cover whole 256-byte row segments.
+//  * wgrad reads packed, transposed, group-padded copies of G and X; row chunks
+//    of a split expert write fp32 partials that a second kernel adds in chunk
+//    order (a fixed-order split of the reduction).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
