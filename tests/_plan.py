@@ -1,0 +1,32 @@
+"""The fwd/dgrad work plan restated for tests: how many 256 x 256 units a call
+has and which of them the tail split cuts (so tests can assert which cases
+exercise a split).  Mirrors the rule the C ABI header documents: with U units,
+T = U mod 256 tail units are cut into S = min(256 // T, 8, groups of 4
+reduction stages, slots // T) pieces when S >= 2."""
+import math
+
+BALANCE, MAX_SPLIT = 256, 8
+
+
+def units(op, sizes, N, K):
+    n_j = N // 256 if op == "fwd" else math.ceil(K / 256)
+    return sum(math.ceil(int(m) / 256) for m in sizes) * n_j
+
+
+def slots(op, M, N, K, E):
+    n_j = N // 256 if op == "fwd" else math.ceil(K / 256)
+    return min(BALANCE, MAX_SPLIT * (math.ceil(M / 256) + E) * n_j)
+
+
+def tail_plan(op, sizes, N, K, M=None, E=None):
+    """(U, T, S): T split units of S pieces each, (U, 0, 1) when nothing is split."""
+    M = int(sum(int(m) for m in sizes)) if M is None else M
+    E = len(sizes) if E is None else E
+    U = units(op, sizes, N, K)
+    T = U % BALANCE
+    if T == 0:
+        return U, 0, 1
+    red = K if op == "fwd" else N
+    groups = (red // 32 + 3) // 4
+    S = min(BALANCE // T, MAX_SPLIT, groups, slots(op, M, N, K, E) // T)
+    return (U, T, S) if S >= 2 else (U, 0, 1)
