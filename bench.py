@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral",
                     choices=["tiny", "mixtral", "fine", "skewed", "stress"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-autograd", action="store_true",
+                    help="skip timing the same step through the autograd wrapper")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -136,6 +138,46 @@ def cpu_baseline(d, target_s: float):
         "sample": (f"experts {used[0][0]}..{used[-1][0]} ({len(used)} experts, {rows} rows) of the "
                    f"workload, fwd+dgrad+wgrad in fp64 NumPy, {spent:.1f} s"),
     }
+
+
+def time_autograd(mdg, d, steps: int, warmup: int, direct_ms: float, flop_op: float) -> dict:
+    """The same step through cake_grouped_det_mm: forward, then a backward with
+    the fused fp32 accumulate into w.main_grad (Megatron placeholder for w.grad).
+    Timed after the main measurement; it does not enter `value`."""
+    import time as _time
+
+    import torch
+
+    x = d["x"].detach().requires_grad_()
+    w = d["w"].detach().requires_grad_()
+    w.main_grad = d["main_grad"]
+    w.grad_added_to_main_grad = False
+    g, offs = d["g"], d["offs"]
+
+    def one():
+        x.grad = None
+        w.grad = None
+        y = mdg.cake_grouped_det_mm(x, w, offs, fuse_wgrad_accumulation=True)
+        y.backward(g)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = _time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        one()
+    stop.record()
+    torch.cuda.synchronize()
+    wall = _time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    return {"ms_per_step": round(ms, 4), "tflops": round(3 * flop_op / (ms * 1e-3) / 1e12, 1),
+            "overhead_vs_direct_pct": round(100.0 * (ms / direct_ms - 1.0), 2),
+            "host_wall_ms_per_step": round(1e3 * wall / steps, 4),
+            "step": "cake_grouped_det_mm forward + backward: dgrad, wgrad fused into fp32 w.main_grad, "
+                    "zero fill of the padding rows of Y and dX, placeholder w.grad"}
 
 
 def main():
@@ -244,6 +286,10 @@ def main():
                 "arithmetic_intensity": round(flop_op / alg_bytes[dom], 1),
                 "hbm_gbs_at_algorithmic_bytes": round(alg_bytes[dom] / (op_ms[dom] * 1e-3) / 1e9, 1)}
 
+    autograd = None
+    if not args.no_autograd:
+        autograd = time_autograd(mdg, d, args.steps, max(args.warmup, 1), ms_per_step, flop_op)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(d, args.cpu_seconds)
@@ -268,6 +314,7 @@ def main():
         "ops": ops,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "autograd": autograd,
         "rerun_bitwise": rerun_ok,
         "wall_s_timed": round(wall, 3),
     }

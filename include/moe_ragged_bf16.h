@@ -13,10 +13,11 @@
  * with all operands bf16, products summed in fp32 in one fixed order (no atomics),
  * so every output is bitwise identical from run to run on one device with one
  * build.  An expert with no rows gets an exactly-zero (+0.0) dW.  wgrad can
- * instead accumulate into an fp32 dW (a Megatron-style main_grad):
- * dW[e] = RN32(dW[e] + G_e^T X_e), one IEEE fp32 add of the finished product per
- * element, bitwise equal to adding this library's own overwrite dW (flashinfer
- * PR #8924, "Design and numerics").
+ * instead accumulate into dW (a Megatron-style main_grad), bitwise equal to
+ * adding this library's own overwrite dW in dW's dtype (flashinfer PR #8924,
+ * "Design and numerics"): fp32, dW[e] = RN32(dW[e] + G_e^T X_e), one IEEE fp32
+ * add of the finished product per element; bf16, the bf16 overwrite result is
+ * added in bf16: RNE_bf16(RN32(dW[e] + RNE_bf16(G_e^T X_e))).
  *
  * Common conventions of every entry point below:
  *
@@ -58,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MDG_ABI_VERSION 2
+#define MDG_ABI_VERSION 3
 
 typedef enum {
   MDG_OK = 0,
@@ -138,10 +139,11 @@ size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t
  *   g [m_rows, n] bf16, read.   x [m_rows, k] bf16, read.   offs [num_groups] int32, read.
  *   dw [num_groups, n, k] of dw_dtype (MDG_BF16 or MDG_FP32):
  *      accumulate == 0: written; an expert with no rows gets +0.0 everywhere.
- *      accumulate != 0: dw_dtype must be MDG_FP32; read and written as
- *        dw = RN32(dw + dW_e) (the add is done for empty experts too, so -0.0
- *        becomes +0.0 as an add of the zero dW would make it).  m_rows == 0 then
- *        enqueues nothing and leaves dw unchanged.
+ *      accumulate != 0: read and written as dw = RN32(dw + dW_e) (MDG_FP32) or
+ *        dw = RNE_bf16(RN32(dw + RNE_bf16(dW_e))) (MDG_BF16: both bf16 values
+ *        widen exactly, one fp32 add, one rounding).  The add is done for empty
+ *        experts too, so -0.0 becomes +0.0 as an add of the zero dW would make
+ *        it.  m_rows == 0 then enqueues nothing and leaves dw unchanged.
  *   workspace: device buffer of at least grouped_det_gemm_wgrad_workspace_bytes()
  *      bytes, 256-byte aligned, owned by the caller, contents on entry ignored;
  *      must not overlap any other argument.  Two calls that share a workspace must
@@ -163,6 +165,22 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
  */
 int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
                                           int32_t num_groups);
+
+/*
+ * Zero fill of the rows that belong to no group: out[r, :] = 0 for
+ * offs[num_groups-1] <= r < m_rows (Cake ragged BF16 grouped GEMM API page,
+ * introduction: groups are consecutive row ranges ending at offs[E-1]; the row
+ * padding case of flashinfer PR #8924, "Tests").  fwd and dgrad leave those
+ * rows untouched; an autograd wrapper uses this to give them a defined value
+ * (zero: they depend on no input) without the host reading offs.
+ *   out [m_rows, row_bytes] bytes, row-major, 16-byte aligned; row_bytes a
+ *     positive multiple of 16 (at most 2^24).  Written only in the rows named.
+ *   offs [num_groups] int32 on the device; only offs[num_groups-1] is read,
+ *     clamped to [0, m_rows].  An m_indptr caller passes m_indptr + 1.
+ * m_rows == 0 enqueues nothing.  out must not overlap offs.
+ */
+int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
+                                   int32_t num_groups, void* stream);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ EXPORTED = (
     "grouped_det_gemm_wgrad",
     "grouped_det_gemm_wgrad_workspace_bytes",
     "grouped_det_gemm_wgrad_chunk_rows",
+    "grouped_det_gemm_zero_pad_rows",
 )
 
 _lock = threading.Lock()
@@ -70,6 +71,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.grouped_det_gemm_wgrad_workspace_bytes.argtypes = [i64, i64, i64, i32]
         lib.grouped_det_gemm_wgrad_chunk_rows.restype = i64
         lib.grouped_det_gemm_wgrad_chunk_rows.argtypes = [i64, i64, i64, i32]
+        lib.grouped_det_gemm_zero_pad_rows.restype = ctypes.c_int
+        lib.grouped_det_gemm_zero_pad_rows.argtypes = [vp, vp, i64, i64, i32, vp]
         _lib = lib
         return lib
 

@@ -272,7 +272,6 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
   int st = check_sizes(m_rows, n, k, num_groups);
   if (st != MDG_OK) return st;
   if (dw_dtype != MDG_BF16 && dw_dtype != MDG_FP32) return MDG_EINVAL;
-  if (accumulate != 0 && dw_dtype != MDG_FP32) return MDG_EUNSUPPORTED;
   if (!offs || !dw || (m_rows > 0 && (!g || !x))) return MDG_EINVAL;
   if (!aligned16(g) || !aligned16(x) || !aligned4(offs) || !aligned16(dw)) return MDG_EINVAL;
   const size_t need = grouped_det_gemm_wgrad_workspace_bytes(m_rows, n, k, num_groups);
@@ -338,6 +337,29 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
     if (split_ub > 65535) return MDG_EUNSUPPORTED;
     if (launch_wgrad_reduce(p, (int)gx, (int)split_ub, s) != hipSuccess) return MDG_EHIP;
   }
+  return MDG_OK;
+}
+
+int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
+                                   int32_t num_groups, void* stream) {
+  if (m_rows < 0 || row_bytes <= 0 || num_groups <= 0) return MDG_EINVAL;
+  if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
+  if (row_bytes % 16 != 0 || m_rows > kMaxRows || row_bytes > (int64_t)1 << 24) return MDG_EUNSUPPORTED;
+  if (!offs || (m_rows > 0 && !out)) return MDG_EINVAL;
+  if (!aligned16(out) || !aligned4(offs)) return MDG_EINVAL;
+  if (overlaps(range_of(out, m_rows * row_bytes), range_of(offs, (int64_t)num_groups * 4))) return MDG_EOVERLAP;
+  if (m_rows == 0) return MDG_OK;
+
+  DeviceInfo dev;
+  const int st = query_device(&dev);
+  if (st != MDG_OK) return st;
+  if (!dev.gfx950) return MDG_EUNSUPPORTED;
+  const int64_t vecs = m_rows * (row_bytes / 16);
+  const int64_t cap = 2 * (int64_t)(dev.cus > 0 ? dev.cus : 256);
+  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cap, (vecs + kThreads - 1) / kThreads));
+  if (launch_zero_rows(out, offs + (num_groups - 1), m_rows, row_bytes, grid, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MDG_EHIP;
   return MDG_OK;
 }
 

@@ -37,7 +37,7 @@ struct GemmParams {
   int32_t n, k, num_groups;
   int32_t chunk_rows;     // wgrad rows per chunk
   int32_t out_fp32;       // wgrad: dW is fp32
-  int32_t accumulate;     // wgrad: dW = RN32(dW + product)
+  int32_t accumulate;     // wgrad: fp32 dW = RN32(dW + product); bf16 dW = RNE(RN32(dW + RNE(product)))
   const uint16_t* gt;     // wgrad: G^T [n, ldp], groups zero-padded to kGroupPad rows (workspace)
   const uint16_t* xt;     // wgrad: X^T [k, ldp], same layout (workspace)
   int64_t ldp;            // wgrad: row length of gt / xt (elements)
@@ -67,6 +67,8 @@ hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream)
 hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream);
 hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
+hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, int64_t row_bytes, int grid,
+                            hipStream_t stream);
 
 // Host-side sizing helpers (capi.cpp).
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);

@@ -478,8 +478,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Epilogue store modes.
-enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2 };
+// bf16 pair + bf16 pair, each element RNE_bf16(RN32(f32(a) + f32(b))): both
+// widen exactly to fp32, one IEEE fp32 add, one rounding to bf16.
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
+  const float lo = __fadd_rn(__uint_as_float(a << 16), __uint_as_float(b << 16));
+  const float hi = __fadd_rn(__uint_as_float(a & 0xffff0000u), __uint_as_float(b & 0xffff0000u));
+  return pack_bf16x2(lo, hi);
+}
+
+// Epilogue store modes: plain stores, and the read-modify-write of an
+// accumulating wgrad (fp32: RN32(out + dW); bf16: the bf16 dW added in bf16).
+enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2, kStoreBf16Acc = 3 };
+
+constexpr bool is_bf16_mode(int mode) { return mode == kStoreBf16 || mode == kStoreBf16Acc; }
 
 // Byte offset that the buffer range check rejects: a load returns 0 and a store
 // is dropped.  Masked lanes use it, so every wave issues the same instructions.
@@ -626,7 +637,7 @@ __device__ __forceinline__ void unstage_slab(u32x4 (&v)[8], const Staging& x) {
 // Vector memory operations one wave issues in the epilogue of each mode.
 template <int mode>
 constexpr int epilogue_ops() {
-  return mode == kStoreBf16 ? 32 : mode == kStoreF32 ? 64 : 128;
+  return mode == kStoreBf16 ? 32 : mode == kStoreF32 || mode == kStoreBf16Acc ? 64 : 128;
 }
 
 // Stores the wave's sub-tile (bf16 or fp32).
@@ -677,6 +688,38 @@ __device__ __forceinline__ void epilogue_accumulate(const Acc& acc, const OutTil
       o[2] = __fadd_rn(o[2], n[2]);
       o[3] = __fadd_rn(o[3], n[3]);
       __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, jh), 0, 0);
+    }
+  }
+}
+
+// dst = RNE_bf16(RN32(f32(dst) + f32(RNE_bf16(acc)))) over the wave's bf16
+// sub-tile: the dW tile is rounded to bf16 first (the overwrite result), then
+// added to the destination the way two bf16 tensors are added.  The
+// destination reads of the next slab are in flight while the current one is
+// staged and added.
+__device__ __forceinline__ void epilogue_accumulate_bf16(const Acc& acc, const OutTile& t, uint8_t* xb,
+                                                         int lane) {
+  const Staging x = staging(xb, lane, true);
+  u32x4 old[2][8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, 0);
+#pragma unroll
+  for (int ib = 0; ib < 4; ++ib) {
+    __builtin_amdgcn_sched_barrier(0);  // one slab at a time (bounds the registers in use)
+    if (ib + 1 < 4) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        old[(ib + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, ib + 1, q, 0), 0, 0);
+    }
+    stage_slab<kStoreBf16>(acc, x, ib, 0);
+    u32x4 v[8];
+    unstage_slab(v, x);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      u32x4 o = old[ib & 1][q];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = add_bf16x2(o[c], v[q][c]);
+      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, 0), 0, 0);
     }
   }
 }
@@ -758,7 +801,7 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
       x.mode = p.accumulate ? kStoreF32Acc : kStoreF32;
     } else {
       x.out = static_cast<uint16_t*>(p.out) + (int64_t)e * N * K + (int64_t)i0 * K + j0;
-      x.mode = kStoreBf16;
+      x.mode = p.accumulate ? kStoreBf16Acc : kStoreBf16;
     }
   }
   return x;
@@ -996,8 +1039,13 @@ __device__ __forceinline__ int run_epilogue(const Acc& acc, const Unit& cur, con
     return epilogue_ops<kStoreF32>();
   } else {
     if (rmw) {
-      epilogue_accumulate(acc, ot, xb, lane);
-      return epilogue_ops<kStoreF32Acc>();
+      if constexpr (OUT == kStoreBf16Acc) {
+        epilogue_accumulate_bf16(acc, ot, xb, lane);
+        return epilogue_ops<kStoreBf16Acc>();
+      } else {
+        epilogue_accumulate(acc, ot, xb, lane);
+        return epilogue_ops<kStoreF32Acc>();
+      }
     }
     if (OUT == kStoreBf16 && cur.mode == kStoreBf16) {
       epilogue_store<kStoreBf16>(acc, ot, xb, lane);
@@ -1017,8 +1065,9 @@ __device__ __forceinline__ int run_epilogue(const Acc& acc, const Unit& cur, con
 //     A of stage kt+4 into stage kt's buffer and read the first half of stage
 //     kt+1's fragments while the MFMAs of stage kt's second half run.
 // One barrier per stage, and no MFMA waits on an LDS read.
-// OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or fp32
-// accumulate for wgrad).  Units of split wgrad experts store fp32 partials.
+// OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or their
+// accumulating forms for wgrad).  Units of split wgrad experts store fp32
+// partials.
 template <int OP, int OUT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
   constexpr bool ATC = Pipe<OP>::ATC;
@@ -1065,7 +1114,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll
         for (int x = 0; x < 4; ++x) acc[ib][jb][x] = 0.0f;
 
-    const bool rmw = OUT == kStoreF32Acc && cur.mode == kStoreF32Acc;
+    const bool rmw = (OUT == kStoreF32Acc || OUT == kStoreBf16Acc) && cur.mode == OUT;
     if (cur.nk > 0) {
       bf16x8 fbA[8], fbB[8], fal[4], fah[4];
       int e1 = tail, e2 = 0;
@@ -1102,7 +1151,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     }
     const int ln = lane_here();
     const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, ln,
-                                cur.mode == kStoreBf16 ? 2 : 4);
+                                is_bf16_mode(cur.mode) ? 2 : 4);
     // Waves 0, 1 stage through s_a3, waves 2, 3 through s_b3.  Each branch names
     // its array, so the compiler can tell the staging accesses apart from the
     // stage loads still landing in the other buffers (a pointer selected at run
@@ -1187,10 +1236,16 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(GemmParams p) {
         *out = s;
       }
     } else {
+      u32x2* out = reinterpret_cast<u32x2*>(p.out) + o;
       u32x2 pk;
       pk[0] = pack_bf16x2(s[0], s[1]);
       pk[1] = pack_bf16x2(s[2], s[3]);
-      reinterpret_cast<u32x2*>(p.out)[o] = pk;
+      if (p.accumulate) {
+        const u32x2 old = *out;
+        pk[0] = add_bf16x2(old[0], pk[0]);
+        pk[1] = add_bf16x2(old[1], pk[1]);
+      }
+      *out = pk;
     }
   }
 }
@@ -1232,6 +1287,25 @@ __global__ __launch_bounds__(kThreads) void tail_reduce_kernel(GemmParams p) {
       *reinterpret_cast<u32x4*>(tu.out + (int64_t)row * tu.ldc + col) = pk;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// rows that belong to no group
+// ---------------------------------------------------------------------------
+// Writes zeros over rows t .. m_rows-1 of a [m_rows, row_bytes] output, with t
+// = offs[E-1] read on the device and clamped to [0, m_rows].  16 bytes per
+// thread and iteration over a grid-stride loop; with no such rows every
+// workgroup exits after one load.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const int32_t* last_end,
+                                                             int64_t m_rows, int64_t row_bytes) {
+  int64_t t = *last_end;
+  t = t < 0 ? 0 : (t > m_rows ? m_rows : t);
+  const int64_t begin = t * row_bytes / 16, end = m_rows * row_bytes / 16;
+  u32x4* dst = reinterpret_cast<u32x4*>(out);
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < end;
+       i += (int64_t)gridDim.x * kThreads)
+    dst[i] = z;
 }
 
 // ---------------------------------------------------------------------------
@@ -1308,14 +1382,23 @@ hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream)
     case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16>), g, blk, 0, stream, p); break;
     case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16>), g, blk, 0, stream, p); break;
     case kWgrad:
-      if (!p.out_fp32)
+      if (!p.out_fp32 && !p.accumulate)
         hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16>), g, blk, 0, stream, p);
+      else if (!p.out_fp32)
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16Acc>), g, blk, 0, stream, p);
       else if (!p.accumulate)
         hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32>), g, blk, 0, stream, p);
       else
         hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc>), g, blk, 0, stream, p);
       break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, int64_t row_bytes, int grid,
+                            hipStream_t stream) {
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(grid), dim3(kThreads), 0, stream, static_cast<uint8_t*>(out),
+                     last_end, m_rows, row_bytes);
   return hipGetLastError();
 }
 

@@ -21,7 +21,8 @@ import torch
 from . import _capi
 
 __all__ = ["grouped_det_gemm_fwd", "grouped_det_gemm_dgrad", "grouped_det_gemm_wgrad",
-           "wgrad_workspace_bytes", "wgrad_chunk_rows"]
+           "fwd_workspace_bytes", "dgrad_workspace_bytes", "wgrad_workspace_bytes",
+           "wgrad_chunk_rows", "zero_pad_rows"]
 
 
 def _stream_handle(t: torch.Tensor) -> int:
@@ -52,6 +53,13 @@ def _offs_ptr(offs: torch.Tensor, E: int) -> int:
     if offs.numel() == E + 1:
         return offs.data_ptr() + 4
     raise ValueError(f"offs has {offs.numel()} entries; expected E={E} (offs) or E+1 (m_indptr)")
+
+
+def _written(t: torch.Tensor) -> None:
+    """Bumps the version counter of a caller's tensor the library wrote in
+    place, as an in-place torch op would (inference tensors have none)."""
+    if not t.is_inference():
+        torch.autograd.graph.increment_version(t)
 
 
 def _same_device(*ts):
@@ -92,6 +100,7 @@ def grouped_det_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
     E, N, K2 = w.shape
     if K2 != K:
         raise ValueError(f"x has K={K} but w has K={K2}")
+    given = out is not None
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16, 2)
@@ -106,6 +115,8 @@ def grouped_det_gemm_fwd(x: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
             x.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E,
             ws.data_ptr(), ws.numel(), _stream_handle(x))
     _capi.check("grouped_det_gemm_fwd", st)
+    if given:
+        _written(out)
     return out
 
 
@@ -120,6 +131,7 @@ def grouped_det_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
     E, N2, K = w.shape
     if N2 != N:
         raise ValueError(f"g has N={N} but w has N={N2}")
+    given = out is not None
     if out is None:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=g.device)
     _need(out, "out", torch.bfloat16, 2)
@@ -134,6 +146,8 @@ def grouped_det_gemm_dgrad(g: torch.Tensor, w: torch.Tensor, offs: torch.Tensor,
             g.data_ptr(), w.data_ptr(), op, out.data_ptr(), M, N, K, E,
             ws.data_ptr(), ws.numel(), _stream_handle(g))
     _capi.check("grouped_det_gemm_dgrad", st)
+    if given:
+        _written(out)
     return out
 
 
@@ -151,10 +165,11 @@ def grouped_det_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor,
                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dW[e] = G[s_e:t_e]^T @ X[s_e:t_e], [E, N, K] in bf16 or fp32.
 
-    With ``accumulate=True`` the product is added into ``out`` (fp32):
-    out = RN32(out + dW).  E comes from ``out``, else ``num_groups``, else the
-    length of ``offs``.  ``workspace`` (uint8 device tensor) is allocated when
-    not given.
+    With ``accumulate=True`` the product is added into ``out`` with the bits
+    of ``out.add_(dW)`` for this function's own overwrite dW in out's dtype:
+    fp32, RN32(out + dW); bf16, RNE_bf16(RN32(out + RNE_bf16(dW))).  E comes
+    from ``out``, else ``num_groups``, else the length of ``offs``.
+    ``workspace`` (uint8 device tensor) is allocated when not given.
     """
     if not isinstance(accumulate, bool):
         raise TypeError("accumulate must be a bool")
@@ -172,6 +187,7 @@ def grouped_det_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor,
         E = offs.numel()
     if out_dtype is not None and out is not None and out.dtype != out_dtype:
         raise TypeError("out_dtype must be None or equal to out.dtype")
+    given = out is not None
     if out is None:
         if accumulate:
             raise ValueError("accumulate=True needs out")
@@ -195,4 +211,25 @@ def grouped_det_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor,
             g.data_ptr(), x.data_ptr(), op, out.data_ptr(), dt_code, int(accumulate),
             M, N, K, E, workspace.data_ptr(), workspace.numel(), _stream_handle(g))
     _capi.check("grouped_det_gemm_wgrad", st)
+    if given:
+        _written(out)
+    return out
+
+
+def zero_pad_rows(out: torch.Tensor, offs: torch.Tensor, num_groups: int) -> torch.Tensor:
+    """Writes zeros over the rows of ``out`` [M, C] at or past offs[E-1] (rows
+    that belong to no group), reading offs on the device only."""
+    if not isinstance(out, torch.Tensor) or out.dim() != 2 or out.device.type != "cuda":
+        raise ValueError("out must be a 2-D device tensor")
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    E = int(num_groups)
+    _same_device(out, offs)
+    op = _offs_ptr(offs, E)
+    row_bytes = out.shape[1] * out.element_size()
+    with torch.cuda.device(out.device):
+        st = _capi.load_library().grouped_det_gemm_zero_pad_rows(
+            out.data_ptr(), op, out.shape[0], row_bytes, E, _stream_handle(out))
+    _capi.check("grouped_det_gemm_zero_pad_rows", st)
+    _written(out)
     return out

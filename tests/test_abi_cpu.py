@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mdg_abi_version() == 2
+    assert lib.mdg_abi_version() == 3
     for s in range(6):
         assert mdg.status_string(s)
     assert mdg.status_string(99) == "unknown status"
@@ -121,7 +121,7 @@ def test_wgrad_refusals(lib):
         return f(g, x, o, d, a["dt"], a["acc"], a["M"], a["N"], a["K"], a["E"], a["ws"], a["wsb"], None)
 
     assert call(dt=2) == EINVAL                        # bad dtype code
-    assert call(dt=0, acc=1) == EUNSUP                 # bf16 accumulate is not offered
+    assert call(dt=0, acc=1, ws=0) == EWS              # bf16 accumulate is offered: checks go on
     assert call(ws=0) == EWS                           # no workspace
     assert call(wsb=need - 1) == EWS                   # short workspace
     assert call(ws=WS + 16) == EINVAL                  # workspace alignment
@@ -135,8 +135,32 @@ def test_wgrad_refusals(lib):
     # accumulate over zero rows leaves dW unchanged: nothing enqueued
     need0 = lib.grouped_det_gemm_wgrad_workspace_bytes(0, 256, 256, 4)
     assert call(M=0, acc=1, wsb=need0) == OK
+    assert call(M=0, acc=1, dt=0, wsb=need0) == OK
     assert call(g=0, x=0, M=0, acc=1, wsb=need0) == OK
     assert call(g=0, M=8) == EINVAL
+    assert call(d=A + 64, dt=0, acc=1) == EOVERLAP     # bf16 dW over g
+
+
+def test_zero_pad_rows_refusals(lib):
+    f = lib.grouped_det_gemm_zero_pad_rows
+
+    def call(o=C, offs=D, M=8, rb=512, E=4):
+        return f(o, offs, M, rb, E, None)
+
+    assert call(M=-1) == EINVAL
+    assert call(rb=0) == EINVAL
+    assert call(E=0) == EINVAL
+    assert call(E=1025) == EUNSUP
+    assert call(rb=520) == EUNSUP                      # row bytes % 16
+    assert call(rb=(1 << 24) + 16) == EUNSUP
+    assert call(offs=0) == EINVAL
+    assert call(o=0) == EINVAL
+    assert call(o=C + 8) == EINVAL                     # 16-byte alignment
+    assert call(offs=D + 2) == EINVAL                  # 4-byte alignment
+    assert call(offs=C + 8 * 512 - 4) == EOVERLAP      # offs inside out
+    assert call(offs=C - 12) == EOVERLAP               # offs[3] is out's first 4 bytes
+    assert call(M=0) == OK                             # nothing to do, nothing enqueued
+    assert call(o=0, M=0) == OK
 
 
 def test_chunk_rows_rule(lib):

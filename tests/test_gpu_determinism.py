@@ -104,3 +104,58 @@ def test_two_streams_same_bits():
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), ref.view(torch.int32))
     assert torch.equal(b.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("sizes", [[0, 1000, 3000, 5, 0, 77], [64, 0, 200]])
+def test_accumulate_bf16_equals_adding_own_dw(sizes):
+    """bf16 out: the bf16 overwrite dW added in bf16, bitwise (torch's bf16 add
+    and the oracle's reading of it), run to run; split and unsplit experts."""
+    d = make_inputs(sizes=sizes, N=512, K=320, seed=19, device=DEV, tensors=("x", "g", "main_grad"))
+    print(f"bf16 accumulate: sizes={sizes}", flush=True)
+    mg0 = d["main_grad"].to(torch.bfloat16)
+    mg0[0, :3, :5] = -0.0
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.bfloat16)
+    expect = mg0.clone().add_(dw)
+    outs = []
+    for _ in range(3):
+        mg = mg0.clone()
+        mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=mg, accumulate=True)
+        outs.append(mg)
+    for mg in outs:
+        assert torch.equal(mg.view(torch.int16), expect.view(torch.int16))
+    from _parity import bits
+    import oracle
+    assert np.array_equal(bits(outs[0]), oracle.accumulate_bf16(bits(mg0), bits(dw)))
+
+
+def test_accumulate_bf16_zero_rows_leaves_out_unchanged():
+    E, N, K = 3, 256, 64
+    g = torch.empty((0, N), dtype=torch.bfloat16, device=DEV)
+    x = torch.empty((0, K), dtype=torch.bfloat16, device=DEV)
+    offs = torch.zeros(E, dtype=torch.int32, device=DEV)
+    mg = torch.randn((E, N, K), device=DEV).to(torch.bfloat16)
+    mg[0, 0, 0] = -0.0
+    before = mg.clone()
+    mdg.grouped_det_gemm_wgrad(g, x, offs, out=mg, accumulate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(mg.view(torch.int16), before.view(torch.int16))
+
+
+@pytest.mark.parametrize("dtype,cols", [(torch.bfloat16, 256), (torch.float32, 64), (torch.bfloat16, 8)])
+def test_zero_pad_rows(dtype, cols):
+    M, E = 1000, 4
+    for ends in ([100, 300, 300, 777], [0, 0, 0, 0], [10, 20, 30, 1000], [5, 6, 7, 4000], [5, 6, 7, -3]):
+        out = torch.randn((M, cols), device=DEV).to(dtype)
+        before = out.clone()
+        offs = torch.tensor(ends, dtype=torch.int32, device=DEV)
+        mdg.zero_pad_rows(out, offs, E)
+        t = min(max(ends[-1], 0), M)
+        torch.cuda.synchronize()
+        assert torch.equal(out[:t], before[:t]), ends
+        assert torch.all(out[t:] == 0) and not torch.signbit(out[t:].float()).any(), ends
+    # the m_indptr form reads the same last end
+    out = torch.ones((M, cols), device=DEV).to(dtype)
+    mdg.zero_pad_rows(out, torch.tensor([0, 10, 20, 30, 500], dtype=torch.int32, device=DEV), E)
+    assert torch.all(out[:500] == 1) and torch.all(out[500:] == 0)
+    # no rows: nothing to do
+    mdg.zero_pad_rows(torch.empty((0, cols), dtype=dtype, device=DEV), offs, E)
