@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MDG_ABI_VERSION 3
+#define MDG_ABI_VERSION 4
 
 typedef enum {
   MDG_OK = 0,
@@ -67,7 +67,8 @@ typedef enum {
   MDG_EUNSUPPORTED = 2,  /* shape outside the supported set, or device is not gfx950 */
   MDG_EOVERLAP = 3,      /* an output shares a byte with an input, offs or the workspace */
   MDG_EWORKSPACE = 4,    /* workspace missing or smaller than required */
-  MDG_EHIP = 5           /* the HIP runtime reported an error when enqueueing */
+  MDG_EHIP = 5,          /* the HIP runtime reported an error when enqueueing */
+  MDG_ENOMEM = 6         /* host memory for a prepared launch could not be allocated */
 } mdg_status;
 
 typedef enum { MDG_BF16 = 0, MDG_FP32 = 1 } mdg_dtype;
@@ -181,6 +182,61 @@ int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
  */
 int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
                                    int32_t num_groups, void* stream);
+
+/*
+ * Prepared launches (Cake ragged BF16 grouped GEMM API page, "Prepared
+ * launches": prepare once, launch many times with no allocation and no host
+ * synchronisation, capturable into a graph, still valid after new offsets or
+ * values are written into the bound buffers).
+ *
+ * grouped_det_gemm_prepare_{fwd,dgrad,wgrad} take exactly the arguments of the
+ * one-shot entry of the same operation (without the stream), run all of its
+ * checks and return the same status; on MDG_OK, *launch receives a new
+ * host-side object holding the bound pointers and the computed kernel
+ * parameters (on any error *launch is set to NULL).  It belongs to the caller,
+ * who releases it with grouped_det_gemm_launch_free.  The bound buffers are
+ * not copied or owned: they must stay allocated while the launch may be
+ * enqueued and until the stream has passed the enqueued work.
+ *
+ * grouped_det_gemm_launch enqueues the prepared kernels on `stream` (they run
+ * exactly as the one-shot entry's would, reading offs and the data on the
+ * device at that time): no validation beyond a NULL check and that the current
+ * HIP device is the one current at preparation (else MDG_EINVAL), no
+ * allocation, no synchronisation and no memset or copy, so it may be called
+ * while the stream is being captured into a HIP graph.  Every launch (and
+ * every replay of a graph holding one) computes again; an accumulating wgrad
+ * adds again.  Launches that share a workspace or an output must be ordered on
+ * one stream.  A prepared launch may be used from several threads.
+ */
+typedef struct mdg_launch mdg_launch;
+
+typedef struct {
+  int32_t op;               /* 0 fwd, 1 dgrad, 2 wgrad */
+  int32_t device;           /* HIP device of the preparation */
+  int32_t kernels;          /* kernels one launch enqueues (0: nothing to do) */
+  int32_t gemm_grid;        /* workgroups of the GEMM kernel's persistent grid */
+  int32_t dw_dtype;         /* wgrad: MDG_BF16 or MDG_FP32 */
+  int32_t accumulate;       /* wgrad: 1 if the launch adds into dw */
+  int32_t chunk_rows;       /* wgrad: rows per chunk of the fixed-order row split */
+  int32_t tail_slots;       /* fwd/dgrad: fp32 partial tiles available to the tail split */
+  int64_t workspace_bytes;  /* workspace bytes the launch uses */
+} mdg_launch_info;
+
+int grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y,
+                                 int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                 void* workspace, size_t workspace_bytes, mdg_launch** launch);
+int grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
+                                   int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                   void* workspace, size_t workspace_bytes, mdg_launch** launch);
+int grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
+                                   int dw_dtype, int accumulate,
+                                   int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                   void* workspace, size_t workspace_bytes, mdg_launch** launch);
+int grouped_det_gemm_launch(const mdg_launch* launch, void* stream);
+/* Describes a prepared launch (MDG_EINVAL for NULL arguments). */
+int grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info);
+/* Releases a prepared launch (NULL is ignored).  Work already enqueued is unaffected. */
+void grouped_det_gemm_launch_free(mdg_launch* launch);
 
 #ifdef __cplusplus
 }

@@ -19,3 +19,10 @@ from .ops import (  # noqa: F401
 )
 from .ops import zero_pad_rows  # noqa: F401
 from .autograd import CakeGroupedDetMm, cake_grouped_det_mm  # noqa: F401
+from .launch import (  # noqa: F401
+    ACCUMULATE_MODES,
+    GroupedDetGemmLaunch,
+    prepare_grouped_det_gemm_fwd,
+    prepare_grouped_det_gemm_dgrad,
+    prepare_grouped_det_gemm_wgrad,
+)

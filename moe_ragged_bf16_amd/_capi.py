@@ -11,7 +11,7 @@ import threading
 
 from .build import LIB_PATH
 
-MDG_OK, MDG_EINVAL, MDG_EUNSUPPORTED, MDG_EOVERLAP, MDG_EWORKSPACE, MDG_EHIP = range(6)
+MDG_OK, MDG_EINVAL, MDG_EUNSUPPORTED, MDG_EOVERLAP, MDG_EWORKSPACE, MDG_EHIP, MDG_ENOMEM = range(7)
 MDG_BF16, MDG_FP32 = 0, 1
 
 EXPORTED = (
@@ -25,7 +25,21 @@ EXPORTED = (
     "grouped_det_gemm_wgrad_workspace_bytes",
     "grouped_det_gemm_wgrad_chunk_rows",
     "grouped_det_gemm_zero_pad_rows",
+    "grouped_det_gemm_prepare_fwd",
+    "grouped_det_gemm_prepare_dgrad",
+    "grouped_det_gemm_prepare_wgrad",
+    "grouped_det_gemm_launch",
+    "grouped_det_gemm_launch_info",
+    "grouped_det_gemm_launch_free",
 )
+
+
+class LaunchInfo(ctypes.Structure):
+    """mdg_launch_info of the C header."""
+    _fields_ = [("op", ctypes.c_int32), ("device", ctypes.c_int32), ("kernels", ctypes.c_int32),
+                ("gemm_grid", ctypes.c_int32), ("dw_dtype", ctypes.c_int32), ("accumulate", ctypes.c_int32),
+                ("chunk_rows", ctypes.c_int32), ("tail_slots", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64)]
 
 _lock = threading.Lock()
 _lib = None
@@ -73,6 +87,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.grouped_det_gemm_wgrad_chunk_rows.argtypes = [i64, i64, i64, i32]
         lib.grouped_det_gemm_zero_pad_rows.restype = ctypes.c_int
         lib.grouped_det_gemm_zero_pad_rows.argtypes = [vp, vp, i64, i64, i32, vp]
+        pp = ctypes.POINTER(vp)
+        for name in ("grouped_det_gemm_prepare_fwd", "grouped_det_gemm_prepare_dgrad"):
+            f = getattr(lib, name)
+            f.restype = ctypes.c_int
+            f.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, pp]
+        lib.grouped_det_gemm_prepare_wgrad.restype = ctypes.c_int
+        lib.grouped_det_gemm_prepare_wgrad.argtypes = [vp, vp, vp, vp, ctypes.c_int, ctypes.c_int,
+                                                       i64, i64, i64, i32, vp, sz, pp]
+        lib.grouped_det_gemm_launch.restype = ctypes.c_int
+        lib.grouped_det_gemm_launch.argtypes = [vp, vp]
+        lib.grouped_det_gemm_launch_info.restype = ctypes.c_int
+        lib.grouped_det_gemm_launch_info.argtypes = [vp, ctypes.POINTER(LaunchInfo)]
+        lib.grouped_det_gemm_launch_free.restype = None
+        lib.grouped_det_gemm_launch_free.argtypes = [vp]
         _lib = lib
         return lib
 

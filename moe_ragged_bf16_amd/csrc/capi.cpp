@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <new>
 
 #include "grouped_gemm.h"
 #include "moe_ragged_bf16.h"
@@ -108,9 +109,10 @@ struct DeviceInfo {
 DeviceInfo g_dev[64];
 std::once_flag g_dev_once[64];
 
-int query_device(DeviceInfo* out) {
+int query_device(DeviceInfo* out, int* device) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MDG_EHIP;
+  *device = dev;
   std::call_once(g_dev_once[dev], [dev]() {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
@@ -158,9 +160,31 @@ int persistent_grid(int64_t units_upper_bound, int cus) {
   return g < 1 ? 1 : (int)g;
 }
 
-int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
-                 int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+}  // namespace
+}  // namespace mdg
+
+// A prepared launch: every argument validated, every kernel parameter and grid
+// computed.  Enqueueing it only launches kernels (no checks, no allocation, no
+// synchronisation, no memset), so it can be recorded into a HIP graph.
+struct mdg_launch {
+  int op;                 // mdg::Op
+  int device;             // HIP device current at preparation
+  int dw_dtype, accumulate;
+  mdg::GemmParams p;
+  int gemm_grid;          // 0: nothing to enqueue at all
+  int tail_gx, tail_gy;   // fwd/dgrad tail reduce grid (0: none)
+  mdg::PackParams qg, qx;
+  int pack_grid;          // wgrad packs (0: none)
+  int red_gx, red_gy;     // wgrad chunk reduce (0: none)
+  int64_t workspace_bytes;
+};
+
+namespace mdg {
+namespace {
+
+int prepare_fwd_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
+                      int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                      mdg_launch* l) {
   int st = check_sizes(m_rows, n, k, num_groups);
   if (st != MDG_OK) return st;
   // Row-indexed tensors may be NULL when there are no rows (never dereferenced).
@@ -178,14 +202,19 @@ int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void*
   const Range rws = range_of(workspace, (int64_t)need);
   if (overlaps(ry, ra) || overlaps(ry, rw) || overlaps(ry, ro) || overlaps(ry, rws)) return MDG_EOVERLAP;
   if (overlaps(rws, ra) || overlaps(rws, rw) || overlaps(rws, ro)) return MDG_EOVERLAP;
-  if (m_rows == 0) return MDG_OK;
+
+  *l = mdg_launch{};
+  l->op = op;
+  l->device = -1;
+  l->workspace_bytes = (int64_t)need;
+  if (m_rows == 0) return MDG_OK;  // nothing to enqueue
 
   DeviceInfo dev;
-  st = query_device(&dev);
+  st = query_device(&dev, &l->device);
   if (st != MDG_OK) return st;
   if (!dev.gfx950) return MDG_EUNSUPPORTED;
 
-  GemmParams p{};
+  GemmParams& p = l->p;
   p.a = static_cast<const uint16_t*>(a);
   p.b = static_cast<const uint16_t*>(w);
   p.offs = offs;
@@ -200,81 +229,27 @@ int fwd_or_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void*
   p.tail_head = reinterpret_cast<int32_t*>(ws);
   p.partial = reinterpret_cast<float*>(ws + kTailHeadBytes);
   p.tail_slots = (int32_t)slots;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  const int grid = persistent_grid(units_ub + slots, dev.cus);
-  if (launch_gemm(op, p, grid, s) != hipSuccess) return MDG_EHIP;
+  l->gemm_grid = persistent_grid(units_ub + slots, dev.cus);
   // Split tail units (at most kBalanceSlots / 2 of them, as each has >= 2
   // pieces): the reduce kernel reads the plan the GEMM kernel wrote and exits
   // at once when there is none.
   if (slots >= 2) {
-    const int64_t gy = std::min<int64_t>(kBalanceSlots / 2, slots / 2);
-    if (launch_tail_reduce(p, 8, (int)gy, s) != hipSuccess) return MDG_EHIP;
+    l->tail_gx = 8;
+    l->tail_gy = (int)std::min<int64_t>(kBalanceSlots / 2, slots / 2);
   }
   return MDG_OK;
 }
 
-}  // namespace
-}  // namespace mdg
-
-using namespace mdg;
-
-extern "C" {
-
-int mdg_abi_version(void) { return MDG_ABI_VERSION; }
-
-const char* mdg_status_string(int s) {
-  switch (s) {
-    case MDG_OK: return "ok";
-    case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
-    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 256 == 0, k % 64 == 0, 1 <= groups <= 1024)";
-    case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
-    case MDG_EWORKSPACE: return "workspace missing or too small";
-    case MDG_EHIP: return "HIP runtime error";
-    default: return "unknown status";
-  }
-}
-
-size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
-  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
-  return fwd_dgrad_workspace(kFwd, m_rows, n, k, num_groups);
-}
-
-size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
-  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
-  return fwd_dgrad_workspace(kDgrad, m_rows, n, k, num_groups);
-}
-
-int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
-                         int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
-                         void* stream) {
-  return fwd_or_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, stream);
-}
-
-int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
-                           int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-  return fwd_or_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes, stream);
-}
-
-int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
-  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
-  return wgrad_chunk_rows(m_rows, n, k, num_groups);
-}
-
-size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
-  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
-  return wgrad_workspace(m_rows, n, k, num_groups).total;
-}
-
-int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
-                           int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+int prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype, int accumulate,
+                  int64_t m_rows, int64_t n, int64_t k, int32_t num_groups, void* workspace,
+                  size_t workspace_bytes, mdg_launch* l) {
   int st = check_sizes(m_rows, n, k, num_groups);
   if (st != MDG_OK) return st;
   if (dw_dtype != MDG_BF16 && dw_dtype != MDG_FP32) return MDG_EINVAL;
   if (!offs || !dw || (m_rows > 0 && (!g || !x))) return MDG_EINVAL;
   if (!aligned16(g) || !aligned16(x) || !aligned4(offs) || !aligned16(dw)) return MDG_EINVAL;
-  const size_t need = grouped_det_gemm_wgrad_workspace_bytes(m_rows, n, k, num_groups);
+  const WgradWorkspace wl = wgrad_workspace(m_rows, n, k, num_groups);
+  const size_t need = wl.total;
   if (!workspace || workspace_bytes < need) return MDG_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MDG_EINVAL;
   const int64_t esz = dw_dtype == MDG_FP32 ? 4 : 2;
@@ -285,18 +260,24 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
   const Range rws = range_of(workspace, (int64_t)need);
   if (overlaps(rd, rg) || overlaps(rd, rx) || overlaps(rd, ro) || overlaps(rd, rws)) return MDG_EOVERLAP;
   if (overlaps(rws, rg) || overlaps(rws, rx) || overlaps(rws, ro)) return MDG_EOVERLAP;
+
+  *l = mdg_launch{};
+  l->op = kWgrad;
+  l->device = -1;
+  l->dw_dtype = dw_dtype;
+  l->accumulate = accumulate != 0;
+  l->workspace_bytes = (int64_t)need;
   // An accumulate over zero rows launches nothing and leaves dw unchanged.
   if (m_rows == 0 && accumulate) return MDG_OK;
 
   DeviceInfo dev;
-  st = query_device(&dev);
+  st = query_device(&dev, &l->device);
   if (st != MDG_OK) return st;
   if (!dev.gfx950) return MDG_EUNSUPPORTED;
 
   const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
-  const WgradWorkspace wl = wgrad_workspace(m_rows, n, k, num_groups);
   char* ws = static_cast<char*>(workspace);
-  GemmParams p{};
+  GemmParams& p = l->p;
   p.a = static_cast<const uint16_t*>(g);
   p.b = static_cast<const uint16_t*>(x);
   p.offs = offs;
@@ -316,29 +297,183 @@ int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, vo
   const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
   const int64_t units_ub = tiles * (num_groups + m_rows / r);
   if (units_ub > INT32_MAX) return MDG_EUNSUPPORTED;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
+  if (split_ub > 65535) return MDG_EUNSUPPORTED;
+  const int64_t cus = dev.cus > 0 ? dev.cus : 256;
   if (m_rows > 0) {
     // G^T and X^T packed copies (rows of each group contiguous, zero-padded)
     const int64_t ptiles = p.ldp / 64;
-    const int pgrid = (int)std::min<int64_t>(4 * (int64_t)(dev.cus > 0 ? dev.cus : 256), ptiles * ((n > k ? n : k) / 64));
-    PackParams qg{p, static_cast<const uint16_t*>(g), reinterpret_cast<uint16_t*>(ws + wl.gt_off), (int32_t)n};
-    PackParams qx{p, static_cast<const uint16_t*>(x), reinterpret_cast<uint16_t*>(ws + wl.xt_off), (int32_t)k};
-    if (launch_wgrad_pack(qg, pgrid, s) != hipSuccess) return MDG_EHIP;
-    if (launch_wgrad_pack(qx, pgrid, s) != hipSuccess) return MDG_EHIP;
+    l->pack_grid = (int)std::min<int64_t>(4 * cus, ptiles * ((n > k ? n : k) / 64));
+    l->qg = PackParams{p, static_cast<const uint16_t*>(g), reinterpret_cast<uint16_t*>(ws + wl.gt_off), (int32_t)n};
+    l->qx = PackParams{p, static_cast<const uint16_t*>(x), reinterpret_cast<uint16_t*>(ws + wl.xt_off), (int32_t)k};
   }
-  if (launch_gemm(kWgrad, p, persistent_grid(units_ub, dev.cus), s) != hipSuccess) return MDG_EHIP;
-  const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
+  l->gemm_grid = persistent_grid(units_ub, dev.cus);
   if (split_ub > 0) {
     const int64_t nk4 = n * k / 4;
     int64_t gx = (nk4 + kThreads * 4 - 1) / (kThreads * 4);
-    const int64_t cap = (4 * (int64_t)(dev.cus > 0 ? dev.cus : 256) + split_ub - 1) / split_ub;
+    const int64_t cap = (4 * cus + split_ub - 1) / split_ub;
     if (gx > cap) gx = cap;
     if (gx < 1) gx = 1;
-    if (split_ub > 65535) return MDG_EUNSUPPORTED;
-    if (launch_wgrad_reduce(p, (int)gx, (int)split_ub, s) != hipSuccess) return MDG_EHIP;
+    l->red_gx = (int)gx;
+    l->red_gy = (int)split_ub;
   }
   return MDG_OK;
 }
+
+// Enqueues a prepared launch: nothing but kernel launches.
+int enqueue(const mdg_launch& l, hipStream_t s) {
+  if (l.gemm_grid == 0) return MDG_OK;
+  if (l.pack_grid > 0) {
+    if (launch_wgrad_pack(l.qg, l.pack_grid, s) != hipSuccess) return MDG_EHIP;
+    if (launch_wgrad_pack(l.qx, l.pack_grid, s) != hipSuccess) return MDG_EHIP;
+  }
+  if (launch_gemm(static_cast<Op>(l.op), l.p, l.gemm_grid, s) != hipSuccess) return MDG_EHIP;
+  if (l.tail_gy > 0 && launch_tail_reduce(l.p, l.tail_gx, l.tail_gy, s) != hipSuccess) return MDG_EHIP;
+  if (l.red_gy > 0 && launch_wgrad_reduce(l.p, l.red_gx, l.red_gy, s) != hipSuccess) return MDG_EHIP;
+  return MDG_OK;
+}
+
+int kernels_of(const mdg_launch& l) {
+  if (l.gemm_grid == 0) return 0;
+  return 1 + (l.pack_grid > 0 ? 2 : 0) + (l.tail_gy > 0) + (l.red_gy > 0);
+}
+
+}  // namespace
+}  // namespace mdg
+
+using namespace mdg;
+
+extern "C" {
+
+int mdg_abi_version(void) { return MDG_ABI_VERSION; }
+
+const char* mdg_status_string(int s) {
+  switch (s) {
+    case MDG_OK: return "ok";
+    case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
+    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 256 == 0, k % 64 == 0, 1 <= groups <= 1024)";
+    case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
+    case MDG_EWORKSPACE: return "workspace missing or too small";
+    case MDG_EHIP: return "HIP runtime error";
+    case MDG_ENOMEM: return "host memory allocation failed";
+    default: return "unknown status";
+  }
+}
+
+size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return fwd_dgrad_workspace(kFwd, m_rows, n, k, num_groups);
+}
+
+size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return fwd_dgrad_workspace(kDgrad, m_rows, n, k, num_groups);
+}
+
+int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
+                         int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  mdg_launch l;
+  const int st = prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, &l);
+  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+}
+
+int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
+                           int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  mdg_launch l;
+  const int st = prepare_fwd_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes, &l);
+  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+}
+
+int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return wgrad_chunk_rows(m_rows, n, k, num_groups);
+}
+
+size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+  if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
+  return wgrad_workspace(m_rows, n, k, num_groups).total;
+}
+
+int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
+                           int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  mdg_launch l;
+  const int st = prepare_wgrad(g, x, offs, dw, dw_dtype, accumulate, m_rows, n, k, num_groups, workspace,
+                               workspace_bytes, &l);
+  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+int publish(int st, const mdg_launch& l, mdg_launch** out) {
+  if (st != MDG_OK) return st;
+  mdg_launch* h = new (std::nothrow) mdg_launch(l);
+  if (!h) return MDG_ENOMEM;
+  *out = h;
+  return MDG_OK;
+}
+}  // namespace
+
+int grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
+                                 int64_t n, int64_t k, int32_t num_groups, void* workspace,
+                                 size_t workspace_bytes, mdg_launch** launch) {
+  if (!launch) return MDG_EINVAL;
+  *launch = nullptr;
+  mdg_launch l;
+  return publish(prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, &l),
+                 l, launch);
+}
+
+int grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
+                                   int64_t n, int64_t k, int32_t num_groups, void* workspace,
+                                   size_t workspace_bytes, mdg_launch** launch) {
+  if (!launch) return MDG_EINVAL;
+  *launch = nullptr;
+  mdg_launch l;
+  return publish(prepare_fwd_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes,
+                                   &l),
+                 l, launch);
+}
+
+int grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
+                                   int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                   void* workspace, size_t workspace_bytes, mdg_launch** launch) {
+  if (!launch) return MDG_EINVAL;
+  *launch = nullptr;
+  mdg_launch l;
+  return publish(prepare_wgrad(g, x, offs, dw, dw_dtype, accumulate, m_rows, n, k, num_groups, workspace,
+                               workspace_bytes, &l),
+                 l, launch);
+}
+
+int grouped_det_gemm_launch(const mdg_launch* launch, void* stream) {
+  if (!launch) return MDG_EINVAL;
+  if (launch->gemm_grid == 0) return MDG_OK;  // nothing to enqueue
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MDG_EHIP;
+  if (dev != launch->device) return MDG_EINVAL;
+  return enqueue(*launch, static_cast<hipStream_t>(stream));
+}
+
+int grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info) {
+  if (!launch || !info) return MDG_EINVAL;
+  mdg_launch_info r;
+  memset(&r, 0, sizeof(r));
+  r.op = launch->op;
+  r.device = launch->device;
+  r.kernels = kernels_of(*launch);
+  r.gemm_grid = launch->gemm_grid;
+  r.dw_dtype = launch->dw_dtype;
+  r.accumulate = launch->accumulate;
+  r.chunk_rows = launch->op == kWgrad ? launch->p.chunk_rows : 0;
+  r.tail_slots = launch->op == kWgrad ? 0 : launch->p.tail_slots;
+  r.workspace_bytes = launch->workspace_bytes;
+  *info = r;
+  return MDG_OK;
+}
+
+void grouped_det_gemm_launch_free(mdg_launch* launch) { delete launch; }
 
 int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
                                    int32_t num_groups, void* stream) {
@@ -351,7 +486,8 @@ int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_row
   if (m_rows == 0) return MDG_OK;
 
   DeviceInfo dev;
-  const int st = query_device(&dev);
+  int device = -1;
+  const int st = query_device(&dev, &device);
   if (st != MDG_OK) return st;
   if (!dev.gfx950) return MDG_EUNSUPPORTED;
   const int64_t vecs = m_rows * (row_bytes / 16);

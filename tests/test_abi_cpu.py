@@ -17,7 +17,7 @@ from moe_ragged_bf16_amd import _capi
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_ragged_bf16.h")
 
-OK, EINVAL, EUNSUP, EOVERLAP, EWS, EHIP = range(6)
+OK, EINVAL, EUNSUP, EOVERLAP, EWS, EHIP, ENOMEM = range(7)
 
 
 def declared_functions():
@@ -39,8 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mdg_abi_version() == 3
-    for s in range(6):
+    assert lib.mdg_abi_version() == 4
+    for s in range(7):
         assert mdg.status_string(s)
     assert mdg.status_string(99) == "unknown status"
 
@@ -200,3 +200,63 @@ def test_workspace_covers_every_grouping(lib, M, N, K, E):
     for s in cases:
         slots = sum(-(-int(m) // R) for m in s if m > R)
         assert slots * N * K * 4 <= have, (s, R)
+
+
+def _prep(lib, name, *args):
+    h = ctypes.c_void_p(0xdead)
+    st = getattr(lib, name)(*args, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad"])
+def test_prepare_fwd_dgrad_refuses_like_one_shot(lib, op):
+    one = getattr(lib, "grouped_det_gemm_" + op)
+    name = "grouped_det_gemm_prepare_" + op
+    need = getattr(lib, "grouped_det_gemm_%s_workspace_bytes" % op)(8, 256, 256, 4)
+    bad = [dict(M=-1), dict(N=128), dict(K=96), dict(E=1025), dict(a=0), dict(a=A + 8),
+           dict(ws=0), dict(wsb=need - 1), dict(ws=WS + 16), dict(d=A + 16), dict(ws=B)]
+    for kw in bad:
+        a = dict(a=A, w=B, o=C, d=D, M=8, N=256, K=256, E=4, ws=WS, wsb=need)
+        a.update(kw)
+        args = (a["a"], a["w"], a["o"], a["d"], a["M"], a["N"], a["K"], a["E"], a["ws"], a["wsb"])
+        want = one(*args, None)
+        assert want != OK
+        st, h = _prep(lib, name, *args)
+        assert st == want, kw
+        assert h.value is None, kw                     # *launch cleared on error
+    assert getattr(lib, name)(A, B, C, D, 8, 256, 256, 4, WS, need, None) == EINVAL
+
+
+def test_prepare_wgrad_refuses_like_one_shot(lib):
+    need = lib.grouped_det_gemm_wgrad_workspace_bytes(512, 256, 256, 4)
+    for kw in [dict(dt=2), dict(ws=0), dict(wsb=need - 1), dict(d=A + 64), dict(ws=A), dict(N=300)]:
+        a = dict(g=A, x=B, o=C, d=D, dt=1, acc=1, M=512, N=256, K=256, E=4, ws=WS, wsb=need)
+        a.update(kw)
+        args = (a["g"], a["x"], a["o"], a["d"], a["dt"], a["acc"], a["M"], a["N"], a["K"], a["E"], a["ws"], a["wsb"])
+        want = lib.grouped_det_gemm_wgrad(*args, None)
+        assert want != OK
+        st, h = _prep(lib, "grouped_det_gemm_prepare_wgrad", *args)
+        assert st == want and h.value is None, kw
+
+
+def test_launch_null_and_empty_launches(lib):
+    assert lib.grouped_det_gemm_launch(None, None) == EINVAL
+    info = _capi.LaunchInfo()
+    assert lib.grouped_det_gemm_launch_info(None, ctypes.byref(info)) == EINVAL
+    lib.grouped_det_gemm_launch_free(None)             # ignored
+    # zero rows: prepared without touching a device; launching enqueues nothing
+    need0 = lib.grouped_det_gemm_fwd_workspace_bytes(0, 256, 256, 4)
+    st, h = _prep(lib, "grouped_det_gemm_prepare_fwd", 0, B, C, 0, 0, 256, 256, 4, WS, need0)
+    assert st == OK and h.value
+    assert lib.grouped_det_gemm_launch_info(h, None) == EINVAL
+    assert lib.grouped_det_gemm_launch_info(h, ctypes.byref(info)) == OK
+    assert (info.op, info.kernels, info.gemm_grid, info.workspace_bytes) == (0, 0, 0, need0)
+    assert lib.grouped_det_gemm_launch(h, None) == OK
+    lib.grouped_det_gemm_launch_free(h)
+    need0 = lib.grouped_det_gemm_wgrad_workspace_bytes(0, 256, 256, 4)
+    st, h = _prep(lib, "grouped_det_gemm_prepare_wgrad", 0, 0, C, D, 0, 1, 0, 256, 256, 4, WS, need0)
+    assert st == OK
+    assert lib.grouped_det_gemm_launch_info(h, ctypes.byref(info)) == OK
+    assert (info.op, info.kernels, info.accumulate, info.dw_dtype) == (2, 0, 1, 0)
+    assert lib.grouped_det_gemm_launch(h, None) == OK
+    lib.grouped_det_gemm_launch_free(h)
