@@ -35,8 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="mixtral",
-                    choices=["tiny", "mixtral", "fine", "skewed", "stress"])
+    from workloads import CONFIGS
+    ap.add_argument("--workload", default="mixtral", choices=list(CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-autograd", action="store_true",
                     help="skip timing the same step through the autograd wrapper")
@@ -278,9 +278,19 @@ def main():
     }
     kernel_name = {"fwd": "fwd", "dgrad": "dgrad", "wgrad_fp32_accumulate": "wgrad"}[dom]
     traffic = measured_traffic(args.workload, kernel_name)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+    # the kernel's bound: MFMA above the ridge point (peak FLOP/s / peak bytes/s),
+    # HBM below it (then achieved and peak are algorithmic bytes per second)
+    intensity = flop_op / alg_bytes[dom]
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity >= ridge:
+        bound, ach, peak, unit = "mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        bound, unit, peak = "hbm", "GB/s", PEAK_HBM_GBS
+        ach = alg_bytes[dom] / (op_ms[dom] * 1e-3) / 1e9
+    roofline = {"bound": bound, "achieved": round(ach, 1), "peak": peak,
+                "unit": unit, "frac": round(ach / peak, 4),
                 "traffic": traffic, "kernel": dom,
+                "tflops": round(achieved, 1), "ridge_flop_per_byte": round(ridge, 1),
                 "flops_per_launch": flop_op,
                 "algorithmic_bytes_per_launch": alg_bytes[dom],
                 "arithmetic_intensity": round(flop_op / alg_bytes[dom], 1),

@@ -17,7 +17,7 @@ from .ops import (  # noqa: F401
     wgrad_workspace_bytes,
     wgrad_chunk_rows,
 )
-from .ops import zero_pad_rows  # noqa: F401
+from .ops import zero_pad_rows, grouped_mm_bf16  # noqa: F401
 from .autograd import CakeGroupedDetMm, cake_grouped_det_mm  # noqa: F401
 from .launch import (  # noqa: F401
     ACCUMULATE_MODES,

@@ -22,7 +22,7 @@ from . import _capi
 
 __all__ = ["grouped_det_gemm_fwd", "grouped_det_gemm_dgrad", "grouped_det_gemm_wgrad",
            "fwd_workspace_bytes", "dgrad_workspace_bytes", "wgrad_workspace_bytes",
-           "wgrad_chunk_rows", "zero_pad_rows"]
+           "wgrad_chunk_rows", "zero_pad_rows", "grouped_mm_bf16"]
 
 
 def _stream_handle(t: torch.Tensor) -> int:
@@ -233,3 +233,21 @@ def zero_pad_rows(out: torch.Tensor, offs: torch.Tensor, num_groups: int) -> tor
     _capi.check("grouped_det_gemm_zero_pad_rows", st)
     _written(out)
     return out
+
+
+def grouped_mm_bf16(a: torch.Tensor, b: torch.Tensor, m_indptr: torch.Tensor,
+                    out: Optional[torch.Tensor] = None, *, backend: str = "cake") -> torch.Tensor:
+    """The stable grouped GEMM forward: ``out[m_indptr[e]:m_indptr[e+1]] =
+    a[...] @ b[e]^T`` for a [cum_m, K], b [E, N, K] and m_indptr [E + 1] (int32,
+    device, leading zero), bf16 out [cum_m, N] (Cake ragged BF16 grouped GEMM API
+    page, "Stable API opt-in").  Rows past m_indptr[E] are zero.  The only
+    backend is this library's (``backend="cake"``, the name the stable API uses
+    for it); there is no tactic index."""
+    if backend != "cake":
+        raise ValueError(f"grouped_mm_bf16: unknown backend {backend!r} (only 'cake')")
+    if not isinstance(m_indptr, torch.Tensor) or m_indptr.dim() != 1 or \
+            not isinstance(b, torch.Tensor) or b.dim() != 3 or m_indptr.numel() != b.shape[0] + 1:
+        raise ValueError("grouped_mm_bf16: m_indptr must be 1-D with E + 1 entries for b [E, N, K]")
+    y = grouped_det_gemm_fwd(a, b, m_indptr, out=out)
+    zero_pad_rows(y, m_indptr, b.shape[0])
+    return y

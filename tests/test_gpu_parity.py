@@ -113,7 +113,7 @@ def _sample_rows(sizes, per_group, rng):
     return np.array(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["mixtral", "fine"])
+@pytest.mark.parametrize("name", ["mixtral", "fine", "gate_up_e32", "down_e4"])
 def test_full_size_sampled(name):
     d = make_inputs(name, seed=0, device=DEV)
     rng = np.random.default_rng(1)
@@ -148,3 +148,17 @@ def test_full_size_sampled(name):
         Xe = bits(d["x"][s:t])
         ref = oracle.wgrad_expert(Ge, Xe)
         assert block_err(values(got), ref) <= TOL_FP32, (name, e)
+
+
+def test_stable_grouped_mm_bf16():
+    d = make_inputs(sizes=[0, 700, 1, 300, 257], N=512, K=320, extra_rows=4, seed=31, device=DEV)
+    t = 1258
+    y = mdg.grouped_mm_bf16(d["x"], d["w"], d["m_indptr"])
+    ref = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    torch.cuda.synchronize()
+    assert torch.equal(y[:t].view(torch.int16), ref[:t].view(torch.int16))
+    assert torch.all(y[t:].view(torch.int16) == 0)
+    with pytest.raises(ValueError):
+        mdg.grouped_mm_bf16(d["x"], d["w"], d["offs"])            # the stable API takes m_indptr
+    with pytest.raises(ValueError):
+        mdg.grouped_mm_bf16(d["x"], d["w"], d["m_indptr"], backend="cudnn")

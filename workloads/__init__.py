@@ -57,6 +57,19 @@ CONFIGS: Dict[str, Workload] = {
                        "E=256 K=7168 N=2048 M=65536, Zipf(1.5) rank weights over all ranks"),
 }
 
+# The two MoE expert projections whose sizes flashinfer PR #8924 ("Cost") tabulates,
+# at E = 4, 8, 16 and 32: gate_up (N=4096, K=6144) and down (N=6144, K=2048).  The
+# pages give no token count; these use 8192 tokens routed top-2 (M = 16384 rows),
+# multinomial over uniform experts, like the Mixtral-style case.
+for _E in (4, 8, 16, 32):
+    CONFIGS[f"gate_up_e{_E}"] = Workload(
+        f"gate_up_e{_E}", _E, 6144, 4096, 16384, "uniform",
+        f"gate_up projection E={_E} K=6144 N=4096 M=16384 (8192 tokens x top-2), uniform experts")
+    CONFIGS[f"down_e{_E}"] = Workload(
+        f"down_e{_E}", _E, 2048, 6144, 16384, "uniform",
+        f"down projection E={_E} K=2048 N=6144 M=16384 (8192 tokens x top-2), uniform experts")
+del _E
+
 # Stream ids of the per-tensor generators: seed * 16 + id.
 TENSOR_STREAMS = {"x": 1, "w": 2, "g": 3, "main_grad": 4}
 
