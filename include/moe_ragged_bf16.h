@@ -35,9 +35,10 @@
  *    of bounds, but the results are then unspecified.  Rows at or past
  *    offs[E-1] belong to no group: fwd and dgrad leave those output rows
  *    untouched and wgrad ignores them.
- *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 256 with n % 256 == 0,
- *    k >= 64 with k % 64 == 0 (the constraints the API page states for the
- *    stable forward entry, adopted for all three operations).
+ *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 64 with n % 64 == 0,
+ *    k >= 64 with k % 64 == 0.  (The API page states n % 256 == 0 and
+ *    k % 64 == 0 for its stable forward entry; here n only needs 64: the last
+ *    256-wide tile along n may be partial.)
  *  - Ownership.  The caller owns every buffer.  The library allocates and frees
  *    no device memory, never synchronises the stream or the device, keeps no
  *    pointer after returning and reads no device memory on the host.  Inputs and

@@ -28,7 +28,7 @@ constexpr int64_t kMinChunkRows = 256;
 
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   (void)num_groups;
-  const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
+  const int64_t tiles = ((n + kTileI - 1) / kTileI) * ((k + kTileJ - 1) / kTileJ);
   const int64_t want_chunks = (kSplitTargetUnits + tiles - 1) / tiles;
   int64_t r = (m_rows + want_chunks - 1) / want_chunks;
   r = (r + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
@@ -51,7 +51,7 @@ int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_
 // fwd/dgrad: units of the persistent schedule (an upper bound: row tiles of
 // every group, each group's last one possibly partial, times column tiles).
 int64_t fwd_dgrad_units_ub(Op op, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
-  const int64_t n_j = (op == kFwd) ? n / kTileJ : (k + kTileJ - 1) / kTileJ;
+  const int64_t n_j = (op == kFwd) ? (n + kTileJ - 1) / kTileJ : (k + kTileJ - 1) / kTileJ;
   const int64_t row_tiles_ub = (m_rows + kTileI - 1) / kTileI + num_groups;
   return row_tiles_ub * n_j;
 }
@@ -147,7 +147,7 @@ bool overlaps(Range a, Range b) {
 int check_sizes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (m_rows < 0 || n <= 0 || k <= 0 || num_groups <= 0) return MDG_EINVAL;
   if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
-  if (n % kTileI != 0 || k % kKAlign != 0) return MDG_EUNSUPPORTED;
+  if (n % kNAlign != 0 || k % kKAlign != 0) return MDG_EUNSUPPORTED;
   if (m_rows > kMaxRows || n > (1 << 20) || k > (1 << 20) || n * k > INT32_MAX)
     return MDG_EUNSUPPORTED;
   return MDG_OK;
@@ -294,7 +294,7 @@ int prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, i
   p.out_fp32 = dw_dtype == MDG_FP32;
   p.accumulate = accumulate != 0;
 
-  const int64_t tiles = (n / kTileI) * ((k + kTileJ - 1) / kTileJ);
+  const int64_t tiles = ((n + kTileI - 1) / kTileI) * ((k + kTileJ - 1) / kTileJ);
   const int64_t units_ub = tiles * (num_groups + m_rows / r);
   if (units_ub > INT32_MAX) return MDG_EUNSUPPORTED;
   const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
@@ -351,7 +351,7 @@ const char* mdg_status_string(int s) {
   switch (s) {
     case MDG_OK: return "ok";
     case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
-    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 256 == 0, k % 64 == 0, 1 <= groups <= 1024)";
+    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 64 == 0, k % 64 == 0, 1 <= groups <= 1024)";
     case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
     case MDG_EWORKSPACE: return "workspace missing or too small";
     case MDG_EHIP: return "HIP runtime error";

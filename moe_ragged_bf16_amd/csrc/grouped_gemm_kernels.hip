@@ -127,12 +127,12 @@ __device__ __forceinline__ UnitShape unit_shape(const GemmParams& p) {
   UnitShape s;
   if (OP == kFwd) {
     s.n_i = 1;
-    s.n_j = p.n / kTileJ;
+    s.n_j = (p.n + kTileJ - 1) / kTileJ;
   } else if (OP == kDgrad) {
     s.n_i = 1;
     s.n_j = (p.k + kTileJ - 1) / kTileJ;
   } else {
-    s.n_i = p.n / kTileI;
+    s.n_i = (p.n + kTileI - 1) / kTileI;
     s.n_j = (p.k + kTileJ - 1) / kTileJ;
   }
   return s;
@@ -760,8 +760,8 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     x.nk = ((OP == kFwd ? K : N) / kTileR + 3) & ~3;
     if (OP == kFwd) {
       x.a = Operand{A + (int64_t)row0 * K * 2, K * 2, x.i_valid * K * 2, K * 2};        // X rows
-      x.b = Operand{B + ((int64_t)e * N + j0) * K * 2, K * 2, kTileJ * K * 2, K * 2};  // W[e] rows n
-      x.j_valid = kTileJ;
+      x.j_valid = min(kTileJ, N - j0);
+      x.b = Operand{B + ((int64_t)e * N + j0) * K * 2, K * 2, x.j_valid * K * 2, K * 2};  // W[e] rows n
       x.out = static_cast<uint16_t*>(p.out) + (int64_t)row0 * N + j0;
       x.ldc = N;
     } else {
@@ -786,10 +786,10 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     x.j_valid = min(kTileJ, K - j0);
     const uint8_t* GT = reinterpret_cast<const uint8_t*>(p.gt);
     const uint8_t* XT = reinterpret_cast<const uint8_t*>(p.xt);
-    x.a = Operand{GT + ((int64_t)i0 * p.ldp + col) * 2, ld_bytes, kTileI * ld_bytes, red_pad * 2};      // G^T rows n
+    x.i_valid = min(kTileI, N - i0);
+    x.a = Operand{GT + ((int64_t)i0 * p.ldp + col) * 2, ld_bytes, x.i_valid * ld_bytes, red_pad * 2};  // G^T rows n
     x.b = Operand{XT + ((int64_t)j0 * p.ldp + col) * 2, ld_bytes, x.j_valid * ld_bytes, red_pad * 2};  // X^T rows k
     x.nk = ((red_pad / kTileR) + 3) & ~3;
-    x.i_valid = kTileI;
     x.ldc = K;
     const int chunks = group_slices<kWgrad>(gm, p);
     if (chunks > 1) {

@@ -9,12 +9,12 @@ BALANCE, MAX_SPLIT = 256, 8
 
 
 def units(op, sizes, N, K):
-    n_j = N // 256 if op == "fwd" else math.ceil(K / 256)
+    n_j = math.ceil(N / 256) if op == "fwd" else math.ceil(K / 256)
     return sum(math.ceil(int(m) / 256) for m in sizes) * n_j
 
 
 def slots(op, M, N, K, E):
-    n_j = N // 256 if op == "fwd" else math.ceil(K / 256)
+    n_j = math.ceil(N / 256) if op == "fwd" else math.ceil(K / 256)
     return min(BALANCE, MAX_SPLIT * (math.ceil(M / 256) + E) * n_j)
 
 

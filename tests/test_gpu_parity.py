@@ -44,8 +44,8 @@ def _check_full(d, label):
     ry = oracle.fwd(X, W, offs)
     rdx = oracle.dgrad(G, W, offs)
     rdw = oracle.wgrad(G, X, offs)
-    ey = group_errs(values(y)[:Mg], ry[:Mg], sizes)
-    edx = group_errs(values(dx)[:Mg], rdx[:Mg], sizes)
+    ey = group_errs(values(y[:Mg]), ry[:Mg], sizes)
+    edx = group_errs(values(dx[:Mg]), rdx[:Mg], sizes)
     assert max(ey, default=0) <= TOL_BF16, (label, "fwd", ey)
     assert max(edx, default=0) <= TOL_BF16, (label, "dgrad", edx)
     # rows past offs[E-1] are untouched
@@ -89,6 +89,10 @@ def test_tiny_indptr_form():
     ([0, 0, 0], 256, 128, 7),                # every group empty
     ([1000, 3000], 256, 256, 0),             # long groups: wgrad row split
     ([700], 768, 576, 0),                    # one group, several tiles in N and K
+    ([0, 257, 0, 255, 256], 320, 320, 2),    # n not a multiple of 256: partial last tile in n
+    ([700, 3], 64, 64, 1),                   # n = 64: a single partial tile
+    ([1000, 3000], 1088, 256, 0),            # partial n tile with the wgrad row split
+    ([513, 0, 1, 1400], 2880, 2880, 3),      # n = k = 2880 (11.25 tiles of 256)
 ])
 def test_small_ragged_full(sizes, N, K, pad):
     d = make_inputs(sizes=sizes, N=N, K=K, extra_rows=pad, seed=3, device=DEV)
