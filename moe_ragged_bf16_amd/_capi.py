@@ -8,8 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 import threading
+from typing import Optional
 
-from .build import LIB_PATH
+from . import build as _build
 
 MDG_OK, MDG_EINVAL, MDG_EUNSUPPORTED, MDG_EOVERLAP, MDG_EWORKSPACE, MDG_EHIP, MDG_ENOMEM = range(7)
 MDG_BF16, MDG_FP32 = 0, 1
@@ -54,12 +55,14 @@ class MdgError(RuntimeError):
         self.status = status
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load (once) and return the library, with argument types declared."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load (once) and return the library, with argument types declared.  It is
+    required: a missing or unloadable library raises (no fallback exists)."""
     global _lib
     with _lock:
         if _lib is not None:
             return _lib
+        path = path or _build.LIB_PATH
         if not os.path.exists(path):
             raise ImportError(
                 f"{path} is missing: build the HIP library first "

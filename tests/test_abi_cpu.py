@@ -260,3 +260,14 @@ def test_launch_null_and_empty_launches(lib):
     assert (info.op, info.kernels, info.accumulate, info.dw_dtype) == (2, 0, 1, 0)
     assert lib.grouped_det_gemm_launch(h, None) == OK
     lib.grouped_det_gemm_launch_free(h)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No fallback: without the built library every entry raises."""
+    from moe_ragged_bf16_amd import build as _build
+    monkeypatch.setattr(_capi, "_lib", None)
+    monkeypatch.setattr(_build, "LIB_PATH", "/nonexistent/libmoe_ragged_bf16.so")
+    with pytest.raises(ImportError, match="build"):
+        mdg.wgrad_workspace_bytes(512, 256, 256, 4)
+    with pytest.raises(ImportError):
+        mdg.load_library()

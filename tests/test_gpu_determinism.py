@@ -159,3 +159,26 @@ def test_zero_pad_rows(dtype, cols):
     assert torch.all(out[:500] == 1) and torch.all(out[500:] == 0)
     # no rows: nothing to do
     mdg.zero_pad_rows(torch.empty((0, cols), dtype=dtype, device=DEV), offs, E)
+
+
+def test_inference_tensors():
+    """Inference-mode tensors as inputs and as the accumulate target (they have
+    no version counter): same bits as ordinary tensors."""
+    d = make_inputs(sizes=[300, 0, 700], N=256, K=192, seed=25, device=DEV, tensors=("x", "w", "g", "main_grad"))
+    y0 = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    mg0 = d["main_grad"].clone()
+    mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=mg0, accumulate=True)
+    with torch.inference_mode():
+        x, w, g = d["x"].clone(), d["w"].clone(), d["g"].clone()
+        offs = d["offs"].clone()
+        mg = d["main_grad"].clone()
+        assert x.is_inference() and mg.is_inference()
+        y = mdg.grouped_det_gemm_fwd(x, w, offs)
+        mdg.grouped_det_gemm_wgrad(g, x, offs, out=mg, accumulate=True)
+        l = mdg.prepare_grouped_det_gemm_dgrad(g, w, offs)
+        dx = l.launch()
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16))
+    assert torch.equal(mg.view(torch.int32), mg0.view(torch.int32))
+    assert torch.equal(dx[:1000].view(torch.int16),
+                       mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"])[:1000].view(torch.int16))
