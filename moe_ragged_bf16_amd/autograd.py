@@ -41,9 +41,9 @@ not differentiable), and so does ``torch.jit.trace``.  ``torch.compile`` with
 call eagerly outside its graphs.
 
 Memory: a non-contiguous (but valid) main_grad is accumulated through a
-contiguous copy; the wgrad workspace (packed operand copies and, for
-experts split into row chunks, fp32 partial tiles) is allocated per call from
-torch's caching allocator.  Under ``torch.use_deterministic_algorithms(True)``
+contiguous copy; the workspaces (fp32 partial tiles of experts split into row
+chunks and of split tail units) are allocated per call from torch's caching
+allocator.  Under ``torch.use_deterministic_algorithms(True)``
 with ``fill_uninitialized_memory`` torch fills the fresh outputs and the
 placeholder with NaN before the kernels write them (an extra pass over each);
 the results are unchanged.

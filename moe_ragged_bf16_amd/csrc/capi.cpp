@@ -69,13 +69,6 @@ size_t fwd_dgrad_workspace(Op op, int64_t m_rows, int64_t n, int64_t k, int32_t 
   return (size_t)kTailHeadBytes + (size_t)slots * kTileI * kTileJ * sizeof(float);
 }
 
-// Row length of the packed transposed copies: every group padded to kGroupPad
-// rows (sum of padded sizes <= M + (kGroupPad - 1) * E), rounded up to 64.
-int64_t wgrad_packed_ld(int64_t m_rows, int32_t num_groups) {
-  const int64_t rows = m_rows + (int64_t)(kGroupPad - 1) * num_groups;
-  return (rows + 63) / 64 * 64;
-}
-
 namespace {
 
 constexpr size_t kTableBytes = 4096;  // reserved head of the workspace
@@ -83,20 +76,17 @@ constexpr size_t kTableBytes = 4096;  // reserved head of the workspace
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Workspace regions of wgrad, in order: reserved head, fp32 partial tiles of
-// split experts, G^T and X^T packed copies.
+// split experts.
 struct WgradWorkspace {
-  size_t partial_off, gt_off, xt_off, total;
+  size_t partial_off, total;
 };
 
 WgradWorkspace wgrad_workspace(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   WgradWorkspace w;
   const int64_t r = wgrad_chunk_rows(m_rows, n, k, num_groups);
   const int64_t slots = wgrad_max_partial_slots(m_rows, r, num_groups);
-  const int64_t ldp = wgrad_packed_ld(m_rows, num_groups);
   w.partial_off = kTableBytes;
-  w.gt_off = align256(w.partial_off + (size_t)slots * (size_t)n * (size_t)k * sizeof(float));
-  w.xt_off = align256(w.gt_off + (size_t)n * (size_t)ldp * 2);
-  w.total = align256(w.xt_off + (size_t)k * (size_t)ldp * 2);
+  w.total = align256(w.partial_off + (size_t)slots * (size_t)n * (size_t)k * sizeof(float));
   return w;
 }
 
@@ -173,8 +163,6 @@ struct mdg_launch {
   mdg::GemmParams p;
   int gemm_grid;          // 0: nothing to enqueue at all
   int tail_gx, tail_gy;   // fwd/dgrad tail reduce grid (0: none)
-  mdg::PackParams qg, qx;
-  int pack_grid;          // wgrad packs (0: none)
   int red_gx, red_gy;     // wgrad chunk reduce (0: none)
   int64_t workspace_bytes;
 };
@@ -283,9 +271,6 @@ int prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, i
   p.offs = offs;
   p.out = dw;
   p.partial = reinterpret_cast<float*>(ws + wl.partial_off);
-  p.gt = reinterpret_cast<const uint16_t*>(ws + wl.gt_off);
-  p.xt = reinterpret_cast<const uint16_t*>(ws + wl.xt_off);
-  p.ldp = wgrad_packed_ld(m_rows, num_groups);
   p.m_rows = m_rows;
   p.n = (int32_t)n;
   p.k = (int32_t)k;
@@ -300,13 +285,6 @@ int prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, i
   const int64_t split_ub = wgrad_max_split_groups(m_rows, r, num_groups);
   if (split_ub > 65535) return MDG_EUNSUPPORTED;
   const int64_t cus = dev.cus > 0 ? dev.cus : 256;
-  if (m_rows > 0) {
-    // G^T and X^T packed copies (rows of each group contiguous, zero-padded)
-    const int64_t ptiles = p.ldp / 64;
-    l->pack_grid = (int)std::min<int64_t>(4 * cus, ptiles * ((n > k ? n : k) / 64));
-    l->qg = PackParams{p, static_cast<const uint16_t*>(g), reinterpret_cast<uint16_t*>(ws + wl.gt_off), (int32_t)n};
-    l->qx = PackParams{p, static_cast<const uint16_t*>(x), reinterpret_cast<uint16_t*>(ws + wl.xt_off), (int32_t)k};
-  }
   l->gemm_grid = persistent_grid(units_ub, dev.cus);
   if (split_ub > 0) {
     const int64_t nk4 = n * k / 4;
@@ -323,10 +301,6 @@ int prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, i
 // Enqueues a prepared launch: nothing but kernel launches.
 int enqueue(const mdg_launch& l, hipStream_t s) {
   if (l.gemm_grid == 0) return MDG_OK;
-  if (l.pack_grid > 0) {
-    if (launch_wgrad_pack(l.qg, l.pack_grid, s) != hipSuccess) return MDG_EHIP;
-    if (launch_wgrad_pack(l.qx, l.pack_grid, s) != hipSuccess) return MDG_EHIP;
-  }
   if (launch_gemm(static_cast<Op>(l.op), l.p, l.gemm_grid, s) != hipSuccess) return MDG_EHIP;
   if (l.tail_gy > 0 && launch_tail_reduce(l.p, l.tail_gx, l.tail_gy, s) != hipSuccess) return MDG_EHIP;
   if (l.red_gy > 0 && launch_wgrad_reduce(l.p, l.red_gx, l.red_gy, s) != hipSuccess) return MDG_EHIP;
@@ -335,7 +309,7 @@ int enqueue(const mdg_launch& l, hipStream_t s) {
 
 int kernels_of(const mdg_launch& l) {
   if (l.gemm_grid == 0) return 0;
-  return 1 + (l.pack_grid > 0 ? 2 : 0) + (l.tail_gy > 0) + (l.red_gy > 0);
+  return 1 + (l.tail_gy > 0) + (l.red_gy > 0);
 }
 
 }  // namespace

@@ -18,8 +18,7 @@ constexpr int kNAlign = 64;      // n must be a multiple of this (partial 256-wi
 constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
-constexpr int kGroupPad = 32;    // wgrad: each group's rows are zero-padded to a multiple of this
-constexpr int64_t kMaxRows = 4000000;  // m_rows limit (keeps the packed layout's buffer ranges < 2^31)
+constexpr int64_t kMaxRows = 4000000;  // m_rows limit (row indices and group sizes stay well inside int32)
 // fwd/dgrad tail split: the units left over after whole rounds of kBalanceSlots
 // units are cut into up to kMaxSplit consecutive reduction ranges (see the kernels).
 constexpr int kBalanceSlots = 256;
@@ -39,9 +38,6 @@ struct GemmParams {
   int32_t chunk_rows;     // wgrad rows per chunk
   int32_t out_fp32;       // wgrad: dW is fp32
   int32_t accumulate;     // wgrad: fp32 dW = RN32(dW + product); bf16 dW = RNE(RN32(dW + RNE(product)))
-  const uint16_t* gt;     // wgrad: G^T [n, ldp], groups zero-padded to kGroupPad rows (workspace)
-  const uint16_t* xt;     // wgrad: X^T [k, ldp], same layout (workspace)
-  int64_t ldp;            // wgrad: row length of gt / xt (elements)
   int32_t tail_slots;     // fwd/dgrad: partial tiles the workspace holds (0: no tail split)
   int32_t* tail_head;     // fwd/dgrad: kTailHeadBytes of workspace: the tail plan for the reduce kernel
 };
@@ -54,19 +50,9 @@ struct TailUnit {
 };
 static_assert(sizeof(TailUnit) == 24, "tail table entry");
 
-// wgrad pack: dst[c][P_e + r] = src[s_e + r][c] for r < m_e, 0 up to the padded
-// group end (P_e = sum of the padded sizes of the groups before e).
-struct PackParams {
-  GemmParams g;           // offs, m_rows, num_groups, ldp (the rest unused)
-  const uint16_t* src;    // [m_rows, cols] bf16
-  uint16_t* dst;          // [cols, ldp] bf16
-  int32_t cols;           // multiple of 64
-};
-
 // Launchers (grouped_gemm_kernels.hip).  Return the HIP status of the launch.
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
-hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream);
 hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, int64_t row_bytes, int grid,
                             hipStream_t stream);
@@ -75,6 +61,5 @@ hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, 
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);
 int64_t wgrad_max_split_groups(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
 int64_t wgrad_max_partial_slots(int64_t m_rows, int64_t chunk_rows, int32_t num_groups);
-int64_t wgrad_packed_ld(int64_t m_rows, int32_t num_groups);
 
 }  // namespace mdg

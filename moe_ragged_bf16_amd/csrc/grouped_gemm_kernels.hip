@@ -8,7 +8,7 @@
 // All three are one tile GEMM  C[i][j] = sum_r A(i, r) * B(j, r):
 //   fwd    i = row, j = n, r = k:   A = X (r contiguous),   B = W[e] (r contiguous)
 //   dgrad  i = row, j = k, r = n:   A = G (r contiguous),   B = W[e] (j contiguous)
-//   wgrad  i = n,   j = k, r = row: A = G^T, B = X^T (packed copies, r contiguous)
+//   wgrad  i = n,   j = k, r = row: A = G (i contiguous),   B = X (j contiguous)
 //
 // Structure of one launch:
 //  * Offsets are read on the device only.  Each workgroup loads offs into LDS,
@@ -37,9 +37,9 @@
 //    reduction order: results are bitwise reproducible.
 //  * Epilogues pass each wave's results through LDS so that global accesses
 //    cover whole 256-byte row segments.
-//  * wgrad reads packed, transposed, group-padded copies of G and X; row chunks
-//    of a split expert write fp32 partials that a second kernel adds in chunk
-//    order (a fixed-order split of the reduction).
+//  * wgrad reads G and X where they lie, both with the reduction (rows)
+//    strided; row chunks of a split expert write fp32 partials that a second
+//    kernel adds in chunk order (a fixed-order split of the reduction).
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -151,7 +151,6 @@ struct GroupTable {
   int* end;      // [E]     clamped, non-decreasing end row of each group
   int* uprefix;  // [E + 1] exclusive prefix of work units
   int* sprefix;  // [E]     wgrad: exclusive prefix of partial slots (split groups only)
-  int* pprefix;  // [E + 1] wgrad: exclusive prefix of the group sizes padded to kGroupPad
   int* scratch;  // [4]
 };
 
@@ -174,8 +173,8 @@ __device__ int build_group_table(const GemmParams& p, GroupTable tb) {
     endv[q] = run;
   }
   const int before = block_excl_max(run, tb.scratch);
-  int units[4], slots[4], pads[4];
-  int usum = 0, ssum = 0, psum = 0;
+  int units[4], slots[4];
+  int usum = 0, ssum = 0;
   int start = before;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -184,39 +183,30 @@ __device__ int build_group_table(const GemmParams& p, GroupTable tb) {
     const int m = end - start;
     units[q] = 0;
     slots[q] = 0;
-    pads[q] = 0;
     if (e < E) {
       const int sl = group_slices<OP>(m, p);
       units[q] = sl * tiles_per_slice;
       slots[q] = (OP == kWgrad && sl > 1) ? sl : 0;
-      pads[q] = (m + kGroupPad - 1) / kGroupPad * kGroupPad;
       tb.end[e] = end;
     }
     usum += units[q];
     ssum += slots[q];
-    psum += pads[q];
     start = end;
   }
-  int utotal, stotal, ptotal;
+  int utotal, stotal;
   int ub = block_excl_sum(usum, tb.scratch, &utotal);
   int sb = block_excl_sum(ssum, tb.scratch, &stotal);
-  int pb = OP == kWgrad ? block_excl_sum(psum, tb.scratch, &ptotal) : 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int e = 4 * t + q;
     if (e < E) {
       tb.uprefix[e] = ub;
       tb.sprefix[e] = sb;
-      if (OP == kWgrad) tb.pprefix[e] = pb;
     }
     ub += units[q];
     sb += slots[q];
-    pb += pads[q];
   }
-  if (t == 0) {
-    tb.uprefix[E] = utotal;
-    if (OP == kWgrad) tb.pprefix[E] = ptotal;
-  }
+  if (t == 0) tb.uprefix[E] = utotal;
   __syncthreads();
   return utotal;
 }
@@ -779,17 +769,15 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     const int R = p.chunk_rows;
     int red = min(R, gm - c * R);
     red = red < 0 ? 0 : red;
-    const int red_pad = (red + kGroupPad - 1) / kGroupPad * kGroupPad;  // zeros past `red` in the packed copies
     const int i0 = ti * kTileI, j0 = tj * kTileJ;
-    const int64_t col = uniform(tb.pprefix[e]) + (int64_t)c * R;        // first packed row of this chunk
-    const int ld_bytes = (int)(p.ldp * 2);
-    x.j_valid = min(kTileJ, K - j0);
-    const uint8_t* GT = reinterpret_cast<const uint8_t*>(p.gt);
-    const uint8_t* XT = reinterpret_cast<const uint8_t*>(p.xt);
+    const int64_t row0 = gs + (int64_t)c * R;  // first row of this chunk
     x.i_valid = min(kTileI, N - i0);
-    x.a = Operand{GT + ((int64_t)i0 * p.ldp + col) * 2, ld_bytes, x.i_valid * ld_bytes, red_pad * 2};  // G^T rows n
-    x.b = Operand{XT + ((int64_t)j0 * p.ldp + col) * 2, ld_bytes, x.j_valid * ld_bytes, red_pad * 2};  // X^T rows k
-    x.nk = ((red_pad / kTileR) + 3) & ~3;
+    x.j_valid = min(kTileJ, K - j0);
+    // both operands in place, the reduction (rows) strided: rows past the chunk's
+    // end load zeros (their stages are cut at `red` rows)
+    x.a = Operand{A + (row0 * N + i0) * 2, N * 2, red, x.i_valid * 2};  // G rows, columns n
+    x.b = Operand{B + (row0 * K + j0) * 2, K * 2, red, x.j_valid * 2};  // X rows, columns k
+    x.nk = ((red + kTileR - 1) / kTileR + 3) & ~3;
     x.ldc = K;
     const int chunks = group_slices<kWgrad>(gm, p);
     if (chunks > 1) {
@@ -924,9 +912,9 @@ __device__ __forceinline__ uint8_t* stage_b() {
 
 template <int OP>
 struct Pipe {
-  // wgrad reads the packed transposed copies, so only dgrad has a strided operand
-  static constexpr bool ATC = false;
-  static constexpr bool BTC = (OP == kDgrad);
+  // operands with the reduction strided: W in dgrad, G and X in wgrad
+  static constexpr bool ATC = (OP == kWgrad);
+  static constexpr bool BTC = (OP != kFwd);
   uint32_t off_a[4], off_b[4];
   int w, wi, wj, lane;
 
@@ -1075,10 +1063,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
-  __shared__ int s_pprefix[kMaxGroups + 1];
   __shared__ int s_scratch[4];
 
-  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
+  GroupTable tb{s_end, s_uprefix, s_sprefix, s_scratch};
   const int total = uniform(build_group_table<OP>(p, tb));  // (from LDS: make it visibly uniform)
   const UnitShape us = unit_shape<OP>(p);
   const Plan pl = make_plan<OP>(p, total);
@@ -1097,8 +1084,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   pipe.wi = pipe.w >> 1;
   pipe.wj = pipe.w & 1;
   // DMA offsets depend only on the operands' row strides (fixed per launch).
-  const int lda = OP == kFwd ? p.k * 2 : OP == kDgrad ? p.n * 2 : (int)(p.ldp * 2);
-  const int ldb = OP == kWgrad ? (int)(p.ldp * 2) : p.k * 2;
+  const int lda = OP == kFwd ? p.k * 2 : p.n * 2;
+  const int ldb = p.k * 2;
   dma_offsets<ATC>(pipe.off_a, lda, pipe.w, pipe.lane);
   dma_offsets<BTC>(pipe.off_b, ldb, pipe.w, pipe.lane);
 
@@ -1176,11 +1163,10 @@ __global__ __launch_bounds__(kThreads) void wgrad_reduce_kernel(GemmParams p) {
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
-  __shared__ int s_pprefix[kMaxGroups + 1];
   __shared__ int s_scratch[4];
   __shared__ int s_pick[2];
 
-  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
+  GroupTable tb{s_end, s_uprefix, s_sprefix, s_scratch};
   build_group_table<kWgrad>(p, tb);
   const int E = p.num_groups;
   const int t = threadIdx.x;
@@ -1308,73 +1294,7 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const
     dst[i] = z;
 }
 
-// ---------------------------------------------------------------------------
-// wgrad: packed transposed copies of G and X
-// ---------------------------------------------------------------------------
-// dst[c][P_e + r] = src[s_e + r][c] for the m_e rows of group e and zero up to
-// m_e rounded up to kGroupPad, where P_e is the exclusive prefix of the padded
-// sizes.  With the reduction (rows) contiguous and every group's rows starting
-// on a 64-byte boundary, the wgrad tiles read both operands exactly like fwd
-// reads X and W.  Persistent grid over 64 x 64 tiles, transposed through LDS;
-// bound by HBM bandwidth (each element read once and written once).
-__global__ __launch_bounds__(kThreads) void wgrad_pack_kernel(PackParams q) {
-  __shared__ int s_end[kMaxGroups];
-  __shared__ int s_uprefix[kMaxGroups + 1];
-  __shared__ int s_sprefix[kMaxGroups];
-  __shared__ int s_pprefix[kMaxGroups + 1];
-  __shared__ int s_scratch[4];
-  __shared__ __attribute__((aligned(16))) uint16_t s_tile[64][72];
-
-  GroupTable tb{s_end, s_uprefix, s_sprefix, s_pprefix, s_scratch};
-  build_group_table<kWgrad>(q.g, tb);
-  const int E = q.g.num_groups;
-  const int total = s_pprefix[E];
-  const int tiles_c = q.cols / 64;
-  const int tiles = (total + 63) / 64 * tiles_c;
-  const int t = threadIdx.x;
-  for (int u = blockIdx.x; u < tiles; u += gridDim.x) {
-    const int pt = u / tiles_c, ct = u - pt * tiles_c;
-    {  // gather: thread t reads 16 columns of packed row pt*64 + t/4
-      const int pr = t >> 2, c0 = (t & 3) * 16;
-      const int P = pt * 64 + pr;
-      u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
-      if (P < total) {
-        int lo = 0, hi = E - 1;  // smallest e with pprefix[e + 1] > P
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (s_pprefix[mid + 1] > P) hi = mid; else lo = mid + 1;
-        }
-        const int gs = lo == 0 ? 0 : s_end[lo - 1];
-        const int r = P - s_pprefix[lo];
-        if (r < s_end[lo] - gs) {
-          const uint16_t* sp = q.src + (int64_t)(gs + r) * q.cols + ct * 64 + c0;
-          v0 = *reinterpret_cast<const u32x4*>(sp);
-          v1 = *reinterpret_cast<const u32x4*>(sp + 8);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        s_tile[c0 + i][pr] = (uint16_t)(v0[i >> 1] >> ((i & 1) * 16));
-        s_tile[c0 + 8 + i][pr] = (uint16_t)(v1[i >> 1] >> ((i & 1) * 16));
-      }
-    }
-    __syncthreads();
-    {  // scatter: thread t writes 16 packed rows of column ct*64 + t/4
-      const int c = t >> 2, p0 = (t & 3) * 16;
-      uint16_t* dp = q.dst + (int64_t)(ct * 64 + c) * q.g.ldp + pt * 64 + p0;
-      *reinterpret_cast<u32x4*>(dp) = *reinterpret_cast<const u32x4*>(&s_tile[c][p0]);
-      *reinterpret_cast<u32x4*>(dp + 8) = *reinterpret_cast<const u32x4*>(&s_tile[c][p0 + 8]);
-    }
-    __syncthreads();
-  }
-}
-
 }  // namespace
-
-hipError_t launch_wgrad_pack(const PackParams& q, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(wgrad_pack_kernel, dim3(grid), dim3(kThreads), 0, stream, q);
-  return hipGetLastError();
-}
 
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(kThreads);

@@ -183,11 +183,9 @@ def test_workspace_covers_every_grouping(lib, M, N, K, E):
     # partial-tile slots the library provisions: floor(M/R) + #experts with > R rows
     big = min(E, M // (R + 1))
     slots_cap = 0 if big == 0 else M // R + big
-    # workspace = 4 KiB head + partial tiles + packed G^T [N, ldp] and X^T [K, ldp]
-    # (bf16, every group padded to 32 rows)
-    ldp = -(-(M + 31 * E) // 64) * 64
-    assert lib.grouped_det_gemm_wgrad_workspace_bytes(M, N, K, E) >= \
-        4096 + slots_cap * N * K * 4 + 2 * (N + K) * ldp
+    # workspace = 4 KiB head + the fp32 partial tiles (G and X are read in place)
+    assert lib.grouped_det_gemm_wgrad_workspace_bytes(M, N, K, E) == \
+        -(-(4096 + slots_cap * N * K * 4) // 256) * 256
     have = slots_cap * N * K * 4
     rng = np.random.default_rng(M + E)
     cases = [np.full(E, M // E) for _ in range(1)]
