@@ -109,34 +109,39 @@ def cpu_baseline(d, target_s: float):
     flops = 0.0
     spent = 0.0
     used = []
-    s = 0
-    for e, m in enumerate(sizes):
-        m = int(m)
-        t0, t1 = s, s + m
-        s = t1
-        if m == 0:
-            continue
-        X = bits(d["x"][t0:t1])
-        G = bits(d["g"][t0:t1])
-        W = bits(d["w"][e:e + 1])
-        offs = np.array([m], dtype=np.int32)
-        c0 = time.perf_counter()
-        oracle.fwd(X, W, offs)
-        oracle.dgrad(G, W, offs)
-        oracle.wgrad(G, X, offs)
-        spent += time.perf_counter() - c0
-        flops += 3 * 2.0 * m * N * K
-        used.append((e, m))
-        if spent >= target_s:
-            break
+    passes = 0
+    while spent < target_s:  # whole experts in order, again from the first if time is left
+        passes += 1
+        s = 0
+        for e, m in enumerate(sizes):
+            m = int(m)
+            t0, t1 = s, s + m
+            s = t1
+            if m == 0:
+                continue
+            X = bits(d["x"][t0:t1])
+            G = bits(d["g"][t0:t1])
+            W = bits(d["w"][e:e + 1])
+            offs = np.array([m], dtype=np.int32)
+            c0 = time.perf_counter()
+            oracle.fwd(X, W, offs)
+            oracle.dgrad(G, W, offs)
+            oracle.wgrad(G, X, offs)
+            spent += time.perf_counter() - c0
+            flops += 3 * 2.0 * m * N * K
+            if passes == 1:
+                used.append((e, m))
+            if spent >= target_s:
+                break
     rows = sum(m for _, m in used)
+    what = (f"all {len(used)} non-empty experts ({rows} rows), {passes} passes" if passes > 1 else
+            f"experts {used[0][0]}..{used[-1][0]} ({len(used)} experts, {rows} rows)")
     return {
         "value": flops / spent / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"experts {used[0][0]}..{used[-1][0]} ({len(used)} experts, {rows} rows) of the "
-                   f"workload, fwd+dgrad+wgrad in fp64 NumPy, {spent:.1f} s"),
+        "sample": f"{what} of the workload, fwd+dgrad+wgrad in fp64 NumPy, {spent:.1f} s",
     }
 
 
