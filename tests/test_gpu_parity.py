@@ -117,7 +117,7 @@ def _sample_rows(sizes, per_group, rng):
     return np.array(rows, dtype=np.int64)
 
 
-@pytest.mark.parametrize("name", ["mixtral", "fine", "gate_up_e32", "down_e4"])
+@pytest.mark.parametrize("name", ["mixtral", "fine", "skewed", "stress", "gate_up_e32", "down_e4"])
 def test_full_size_sampled(name):
     d = make_inputs(name, seed=0, device=DEV)
     rng = np.random.default_rng(1)
@@ -166,3 +166,44 @@ def test_stable_grouped_mm_bf16():
         mdg.grouped_mm_bf16(d["x"], d["w"], d["offs"])            # the stable API takes m_indptr
     with pytest.raises(ValueError):
         mdg.grouped_mm_bf16(d["x"], d["w"], d["m_indptr"], backend="cudnn")
+
+
+@pytest.mark.parametrize("name", ["mixtral", "stress"])
+def test_adjoint_identity_full_size(name):
+    """<Y, G> = <X, dX> = sum_e <W[e], dW[e]> over the group rows: all three equal
+    sum_e <G_e^T X_e, W[e]>.  Computed in fp64 on the device from the three
+    kernels' outputs at the full workload size; Y and dX are bf16-rounded, so the
+    sides agree to about the bf16 rounding (a wrong index, sign or group in any one
+    kernel breaks the equality by O(1))."""
+    d = make_inputs(name, seed=0, device=DEV)
+    print(f"adjoint identity: {name}", flush=True)
+    t = int(d["sizes"].sum())
+    y = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    dx = mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"])
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)
+    pyg = y[:t].double() * d["g"][:t].double()
+    pxdx = d["x"][:t].double() * dx[:t].double()
+    yg, xdx = torch.sum(pyg).item(), torch.sum(pxdx).item()
+    wdw = sum(torch.sum(d["w"][e].double() * dw[e].double()).item() for e in range(d["E"]))
+    # the bf16 rounding of Y (resp. dX) perturbs each product by ~2^-9 of itself with
+    # random sign: the sums then differ by ~2^-9 * ||products||_2 (the signed sums
+    # themselves are of that norm's order, so an error in any kernel shows as O(1))
+    ny, nx = torch.linalg.vector_norm(pyg).item(), torch.linalg.vector_norm(pxdx).item()
+    print(f"  <Y,G>={yg:.6g} <X,dX>={xdx:.6g} sum<W,dW>={wdw:.6g} "
+          f"|dy|/||YG||={abs(yg - wdw) / ny:.2e} |dx|/||XdX||={abs(xdx - wdw) / nx:.2e}", flush=True)
+    assert abs(yg - wdw) <= 1e-2 * ny, (name, yg, wdw, ny)
+    assert abs(xdx - wdw) <= 1e-2 * nx, (name, xdx, wdw, nx)
+    assert abs(wdw) > 0.05 * ny, (name, wdw, ny)      # the identity is not vacuous here
+
+
+def test_single_group_equals_dense():
+    """E = 1: the grouped ops are plain dense products (fp32 torch matmul as the
+    reference, within the bf16 output tolerance)."""
+    d = make_inputs(sizes=[1000], N=512, K=320, seed=41, device=DEV)
+    x, w, g = d["x"].float(), d["w"][0].float(), d["g"].float()
+    y = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"]).float()
+    dx = mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"]).float()
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=torch.float32)[0]
+    for got, ref, tol in ((y, x @ w.T, TOL_BF16), (dx, g @ w, TOL_BF16), (dw, g.T @ x, TOL_FP32)):
+        err = ((got - ref).abs().max() / ref.abs().max()).item()
+        assert err <= tol, err
