@@ -55,9 +55,9 @@ def _check_full(d, label):
         dw = values(dws[dt])
         errs = [block_err(dw[e], rdw[e]) for e in range(d["E"])]
         assert max(errs) <= tol, (label, "wgrad", dt, errs)
+        raw = dws[dt].cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32)
         for e, m in enumerate(sizes):
             if m == 0:
-                raw = dws[dt].cpu().view(torch.int16 if dt == torch.bfloat16 else torch.int32)
                 assert torch.all(raw[e] == 0), (label, "empty expert must be +0.0", e)
     # bf16 dW is the RNE rounding of the fp32 dW (one shared reduction)
     assert torch.equal(dws[torch.float32].to(torch.bfloat16).view(torch.int16),
@@ -207,3 +207,18 @@ def test_single_group_equals_dense():
     for got, ref, tol in ((y, x @ w.T, TOL_BF16), (dx, g @ w, TOL_BF16), (dw, g.T @ x, TOL_FP32)):
         err = ((got - ref).abs().max() / ref.abs().max()).item()
         assert err <= tol, err
+
+
+@pytest.mark.parametrize("E", [1024, 1000])
+def test_max_group_count(E):
+    """The largest supported number of groups (the LDS group table holds 1024;
+    each of the 256 threads owns 4 entries): mostly empty groups, a few long ones,
+    every element against the oracle."""
+    rng = np.random.default_rng(E)
+    sizes = np.zeros(E, dtype=np.int64)
+    hot = rng.choice(E, 24, replace=False)
+    sizes[hot] = rng.integers(1, 300, 24)
+    sizes[E - 1] = 5                                   # the last group is not empty
+    d = make_inputs(sizes=sizes, N=256, K=128, extra_rows=3, seed=E, device=DEV)
+    print(f"E={E} rows={int(sizes.sum())}", flush=True)
+    _check_full(d, f"E={E}")
