@@ -55,5 +55,24 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi_smoke.cpp")
+C_SMOKE_BIN = os.path.join(ROOT, "tests", "c_abi_smoke")
+
+
+def build_c_smoke(verbose: bool = False) -> str:
+    """Compile the C++ caller of the C ABI used by the tests (host code only,
+    linked against the library with a relative rpath)."""
+    cmd = [hipcc(), "-O2", "-std=c++17", "-I", INCLUDE, C_SMOKE_SRC, "-L", PKG_DIR, "-lmoe_ragged_bf16",
+           "-Wl,-rpath,$ORIGIN/../moe_ragged_bf16_amd", "-o", C_SMOKE_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building %s" % C_SMOKE_BIN)
+    return C_SMOKE_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_smoke(verbose=True))
