@@ -87,6 +87,7 @@ def test_tiny_indptr_form():
     ([0, 257, 0, 255, 256], 512, 320, 0),    # empties, tile +-1, k not a multiple of 256
     ([300, 1, 2, 63, 64, 65], 256, 192, 5),  # row padding past the last group
     ([0, 0, 0], 256, 128, 7),                # every group empty
+    ([0, 0, 0, 0], 896, 576, 0),             # no rows at all (M = 0)
     ([1000, 3000], 256, 256, 0),             # long groups: wgrad row split
     ([700], 768, 576, 0),                    # one group, several tiles in N and K
     ([0, 257, 0, 255, 256], 320, 320, 2),    # n not a multiple of 256: partial last tile in n

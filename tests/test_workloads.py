@@ -67,3 +67,10 @@ def test_make_inputs_custom_and_padding():
     d = make_inputs(sizes=[3, 0, 5], K=64, N=256, extra_rows=4)
     assert d["M"] == 12 and d["x"].shape == (12, 64)
     assert d["offs"].tolist() == [3, 3, 8] and d["m_indptr"].tolist() == [0, 3, 3, 8]
+
+
+def test_make_inputs_without_rows():
+    """Every group empty and no padding: zero-row tensors, offsets all zero."""
+    d = make_inputs(sizes=[0, 0, 0], N=256, K=64, seed=1, tensors=("x", "w", "g", "main_grad"))
+    assert d["M"] == 0 and d["x"].shape == (0, 64) and d["g"].shape == (0, 256)
+    assert d["w"].shape == (3, 256, 64) and d["offs"].tolist() == [0, 0, 0]

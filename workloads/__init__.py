@@ -127,6 +127,8 @@ def _gen(seed: int, stream: int, device) -> torch.Generator:
 def _randn_bf16(shape, scale: float, seed: int, stream: int, device) -> torch.Tensor:
     gen = _gen(seed, stream, device)
     out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    if out.numel() == 0:  # e.g. no rows at all: nothing to draw
+        return out
     # Draw in slabs along dim 0 so that the fp32 staging stays small.
     flat = out.view(shape[0], -1)
     per_row = flat.shape[1]
