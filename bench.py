@@ -192,7 +192,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+              "this benchmark has no multi-GPU mode.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
