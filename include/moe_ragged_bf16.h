@@ -35,10 +35,13 @@
  *    of bounds, but the results are then unspecified.  Rows at or past
  *    offs[E-1] belong to no group: fwd and dgrad leave those output rows
  *    untouched and wgrad ignores them.
- *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 64 with n % 64 == 0,
- *    k >= 64 with k % 64 == 0.  (The API page states n % 256 == 0 and
- *    k % 64 == 0 for its stable forward entry; here n only needs 64: the last
- *    256-wide tile along n may be partial.)
+ *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 8 with n % 8 == 0,
+ *    k >= 8 with k % 8 == 0.  (The API page states n % 256 == 0 and k % 64 == 0
+ *    for its stable forward entry; here both only need multiples of 8, i.e.
+ *    rows of whole 16-byte chunks, the unit of every load and store: the last
+ *    256-wide output tile along n or k may be partial, and a reduction over k
+ *    (fwd) or n (dgrad) that is not a multiple of 32 ends in a partial stage
+ *    whose missing columns load as zeros.)
  *  - Ownership.  The caller owns every buffer.  The library allocates and frees
  *    no device memory, never synchronises the stream or the device, keeps no
  *    pointer after returning and reads no device memory on the host.  Inputs and
@@ -60,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MDG_ABI_VERSION 4
+#define MDG_ABI_VERSION 5
 
 typedef enum {
   MDG_OK = 0,

@@ -325,7 +325,7 @@ const char* mdg_status_string(int s) {
   switch (s) {
     case MDG_OK: return "ok";
     case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
-    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 64 == 0, k % 64 == 0, 1 <= groups <= 1024)";
+    case MDG_EUNSUPPORTED: return "unsupported shape or device (needs gfx950, n % 8 == 0, k % 8 == 0, 1 <= groups <= 1024)";
     case MDG_EOVERLAP: return "an output overlaps an input, the offsets or the workspace";
     case MDG_EWORKSPACE: return "workspace missing or too small";
     case MDG_EHIP: return "HIP runtime error";

@@ -13,8 +13,8 @@ constexpr int kTileI = 256;      // output tile extent along the first output di
 constexpr int kTileJ = 256;      // output tile extent along the unit-stride output dim
 constexpr int kTileR = 32;       // reduction depth of one LDS stage
 constexpr int kStages = 4;       // LDS stages (kStages - 1 in flight)
-constexpr int kKAlign = 64;      // k must be a multiple of this (the ABI's contract)
-constexpr int kNAlign = 64;      // n must be a multiple of this (partial 256-wide tiles are masked)
+constexpr int kKAlign = 8;       // k must be a multiple of this: rows of whole 16-byte chunks
+constexpr int kNAlign = 8;       // n likewise (partial tiles and partial reduction stages are masked)
 constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table

@@ -272,6 +272,20 @@ __device__ __forceinline__ void dma_offsets(uint32_t (&off)[4], int ld_bytes, in
   }
 }
 
+// Byte offset, within the 64-byte stage row of an RC operand, of the 16-byte
+// chunk that each of this wave's 4 loads fetches (used to mask a partial stage).
+__device__ __forceinline__ void dma_chunks_rc(uint32_t (&cb)[4], int w, int lane) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = (q * 4 + w) * 16 + (lane >> 2);
+    cb[q] = (uint32_t)(((lane & 3) ^ swz_rc(row)) * 16);
+  }
+}
+
+// Byte offset that the buffer range check rejects: a load returns 0 and a store
+// is dropped.  Masked lanes use it, so every wave issues the same instructions.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // Operand of one unit: where its data starts and how much of it is real.  The
 // byte ranges handed to the buffer loads never leave the operand's own valid
 // rows, so no load can touch memory past a tensor.
@@ -314,6 +328,18 @@ __device__ __forceinline__ void dma_one(const DmaStage& d, uint32_t off, int q) 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (lds_void*)(d.lds + q * 4096), 16, off, 0, 0, 0);
 }
 
+// Valid bytes of each row of an RC operand's stage kt (64 for a whole stage,
+// fewer in the last stage of a reduction that is not a multiple of 32).
+__device__ __forceinline__ uint32_t stage_valid_bytes(const Operand& o, int kt) {
+  return (uint32_t)min(max(o.aux - kt * kTileR * 2, 0), kTileR * 2);
+}
+
+// dma_one for a possibly partial RC stage: chunks at or past `kv` bytes of the
+// row load zeros instead (the same instruction, with an offset out of range).
+__device__ __forceinline__ void dma_one_masked(const DmaStage& d, uint32_t off, uint32_t cb, uint32_t kv, int q) {
+  dma_one(d, cb < kv ? off : kOutOfRange, q);
+}
+
 // Issues this wave's DMA loads of reduction stage `kt` of one operand into the
 // LDS stage at `lds` (a wave-uniform address: `lds_w` already includes this
 // wave's first segment).  The buffer's range check zero-fills everything past
@@ -342,6 +368,15 @@ __device__ __forceinline__ void dma_stage(const Operand& o, const uint32_t (&off
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds_w + q * 4096), 16, off[q], 0, 0, 0);
+}
+
+// dma_stage of an RC operand whose stage may be partial (see dma_one_masked).
+__device__ __forceinline__ void dma_stage_masked(const Operand& o, const uint32_t (&off)[4], const uint32_t (&cb)[4],
+                                                 uint8_t* lds_w, int kt, bool live) {
+  const DmaStage d = dma_begin<false>(o, lds_w, kt, live);
+  const uint32_t kv = stage_valid_bytes(o, kt);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dma_one_masked(d, off[q], cb[q], kv, q);
 }
 
 // Waits until at most `kVm` of this wave's vector memory operations are
@@ -482,13 +517,9 @@ enum Store : int { kStoreBf16 = 0, kStoreF32 = 1, kStoreF32Acc = 2, kStoreBf16Ac
 
 constexpr bool is_bf16_mode(int mode) { return mode == kStoreBf16 || mode == kStoreBf16Acc; }
 
-// Byte offset that the buffer range check rejects: a load returns 0 and a store
-// is dropped.  Masked lanes use it, so every wave issues the same instructions.
-constexpr uint32_t kOutOfRange = 0x80000000u;
-
 // The output tile of one unit as seen by one wave: rows i < i_valid and
 // columns j < j_valid of the 256 x 256 tile at `out` (row stride ldc elements;
-// j_valid is a multiple of 64).  The epilogue passes the accumulators through
+// j_valid is a multiple of 8, so each lane's 16 bytes are all valid or all not).  The epilogue passes the accumulators through
 // LDS (a "staging" buffer of 8 KiB per wave) so that every global access covers
 // whole 256-byte row segments: one load or store instruction moves 4 rows x 256
 // bytes, 16 bytes per lane, where the MFMA layout itself (lane = row) would give
@@ -748,7 +779,7 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
     const int row0 = gs + rt * kTileI;
     x.i_valid = min(kTileI, gm - rt * kTileI);
     const int j0 = ct * kTileJ;
-    x.nkr = (OP == kFwd ? K : N) / kTileR;
+    x.nkr = ((OP == kFwd ? K : N) + kTileR - 1) / kTileR;
     x.nk = (x.nkr + 3) & ~3;
     if (OP == kFwd) {
       x.a = Operand{A + (int64_t)row0 * K * 2, K * 2, x.i_valid * K * 2, K * 2};        // X rows
@@ -822,7 +853,7 @@ __device__ __forceinline__ Plan make_plan(const GemmParams& p, int total) {
   if (OP == kWgrad || p.tail_slots < 2) return pl;
   const int t = total % kBalanceSlots;
   if (t == 0) return pl;
-  const int groups = ((OP == kFwd ? p.k : p.n) / kTileR + 3) / 4;
+  const int groups = (((OP == kFwd ? p.k : p.n) + kTileR - 1) / kTileR + 3) / 4;
   const int sp = min(min(kBalanceSlots / t, kMaxSplit), min(groups, p.tail_slots / t));
   if (sp < 2) return pl;
   pl.full = total - t;
@@ -914,22 +945,27 @@ __device__ __forceinline__ uint8_t* stage_b() {
   else return s_b3;
 }
 
-template <int OP>
+// MASK: the reduction extent is not a multiple of 32, so the last stage of an
+// RC operand is partial and its loads mask the chunks past the extent.
+template <int OP, bool MASK>
 struct Pipe {
   // operands with the reduction strided: W in dgrad, G and X in wgrad
   static constexpr bool ATC = (OP == kWgrad);
   static constexpr bool BTC = (OP != kFwd);
   uint32_t off_a[4], off_b[4];
+  uint32_t cb_a[4], cb_b[4];  // MASK: chunk byte positions of the RC loads (dma_chunks_rc)
   int w, wi, wj, lane;
 
   // This wave's 4 DMA loads of operand A (resp. B) of stage kt into buffer S.
   template <int S>
   __device__ __forceinline__ void issue_a(const Unit& x, int kt) const {
-    dma_stage<ATC>(x.a, off_a, stage_a<S>() + w * 1024, kt, kt < x.nk);
+    if constexpr (MASK && !ATC) dma_stage_masked(x.a, off_a, cb_a, stage_a<S>() + w * 1024, kt, kt < x.nk);
+    else dma_stage<ATC>(x.a, off_a, stage_a<S>() + w * 1024, kt, kt < x.nk);
   }
   template <int S>
   __device__ __forceinline__ void issue_b(const Unit& x, int kt) const {
-    dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, kt < x.nk);
+    if constexpr (MASK && !BTC) dma_stage_masked(x.b, off_b, cb_b, stage_b<S>() + w * 1024, kt, kt < x.nk);
+    else dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, kt < x.nk);
   }
 
   // Stages 0..2 of a unit into buffers 0..2, and operand A of stage 3.
@@ -973,11 +1009,15 @@ struct Pipe {
     // first half: row blocks 0..3; reads of fah early, operand B of stage kt+3
     // after every second column block
     const DmaStage db = dma_begin<BTC>(x.b, stage_b<S3>() + w * 1024, kt + 3, kt + 3 < x.nk);
+    const uint32_t kvb = MASK && !BTC ? stage_valid_bytes(x.b, kt + 3) : 0;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
       mma_col(acc, fbc[jb], fal, 0, jb);
       if (jb < 4) fah[jb] = load_frag<ATC>(stage_a<S>(), wi * 128 + 64 + 16 * jb, lane);
-      if (jb & 1) dma_one(db, off_b[jb >> 1], jb >> 1);
+      if (jb & 1) {
+        if constexpr (MASK && !BTC) dma_one_masked(db, off_b[jb >> 1], cb_b[jb >> 1], kvb, jb >> 1);
+        else dma_one(db, off_b[jb >> 1], jb >> 1);
+      }
     }
     if constexpr (kFirst) {
       wait_vm(2 * kDmaPerStage + e2 + e1);  // stage kt+1 has landed
@@ -991,6 +1031,7 @@ struct Pipe {
     // half consumes them (fb[0], fa[0..3], fb[1..7]), operand A of stage kt+4
     // into stage kt's buffer (after the last stage these reads are discarded)
     const DmaStage da = dma_begin<ATC>(x.a, stage_a<S>() + w * 1024, kt + 4, kt + 4 < x.nk);
+    const uint32_t kva = MASK && !ATC ? stage_valid_bytes(x.a, kt + 4) : 0;
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) {
       mma_col(acc, fbc[jb], fah, 4, jb);
@@ -1003,7 +1044,10 @@ struct Pipe {
       } else {
         fbn[jb] = load_frag<BTC>(stage_b<S1>(), wj * 128 + 16 * jb, lane);
       }
-      if (jb & 1) dma_one(da, off_a[jb >> 1], jb >> 1);
+      if (jb & 1) {
+        if constexpr (MASK && !ATC) dma_one_masked(da, off_a[jb >> 1], cb_a[jb >> 1], kva, jb >> 1);
+        else dma_one(da, off_a[jb >> 1], jb >> 1);
+      }
     }
   }
 
@@ -1060,10 +1104,10 @@ __device__ __forceinline__ int run_epilogue(const Acc& acc, const Unit& cur, con
 // OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or their
 // accumulating forms for wgrad).  Units of split wgrad experts store fp32
 // partials.
-template <int OP, int OUT>
+template <int OP, int OUT, bool MASK>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
-  constexpr bool ATC = Pipe<OP>::ATC;
-  constexpr bool BTC = Pipe<OP>::BTC;
+  constexpr bool ATC = Pipe<OP, MASK>::ATC;
+  constexpr bool BTC = Pipe<OP, MASK>::BTC;
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
@@ -1082,7 +1126,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int bid = blockIdx.x;
   const int vb = (P % 8 == 0) ? (bid % 8) * (P / 8) + bid / 8 : bid;
 
-  Pipe<OP> pipe;
+  Pipe<OP, MASK> pipe;
   pipe.lane = threadIdx.x & 63;
   pipe.w = uniform(threadIdx.x >> 6);
   pipe.wi = pipe.w >> 1;
@@ -1092,6 +1136,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int ldb = p.k * 2;
   dma_offsets<ATC>(pipe.off_a, lda, pipe.w, pipe.lane);
   dma_offsets<BTC>(pipe.off_b, ldb, pipe.w, pipe.lane);
+  if constexpr (MASK) {
+    dma_chunks_rc(pipe.cb_a, pipe.w, pipe.lane);
+    dma_chunks_rc(pipe.cb_b, pipe.w, pipe.lane);
+  }
 
   Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
   if (cur.valid) pipe.prefetch(cur);
@@ -1316,17 +1364,23 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(kThreads);
   switch (op) {
-    case kFwd: hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16>), g, blk, 0, stream, p); break;
-    case kDgrad: hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16>), g, blk, 0, stream, p); break;
+    case kFwd:  // the reduction is k
+      if (p.k % kTileR == 0) hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, false>), g, blk, 0, stream, p);
+      else hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, true>), g, blk, 0, stream, p);
+      break;
+    case kDgrad:  // the reduction is n
+      if (p.n % kTileR == 0) hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, false>), g, blk, 0, stream, p);
+      else hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, true>), g, blk, 0, stream, p);
+      break;
     case kWgrad:
       if (!p.out_fp32 && !p.accumulate)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16, false>), g, blk, 0, stream, p);
       else if (!p.out_fp32)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16Acc>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16Acc, false>), g, blk, 0, stream, p);
       else if (!p.accumulate)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32, false>), g, blk, 0, stream, p);
       else
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc, false>), g, blk, 0, stream, p);
       break;
   }
   return hipGetLastError();

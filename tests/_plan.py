@@ -27,6 +27,6 @@ def tail_plan(op, sizes, N, K, M=None, E=None):
     if T == 0:
         return U, 0, 1
     red = K if op == "fwd" else N
-    groups = (red // 32 + 3) // 4
+    groups = ((red + 31) // 32 + 3) // 4
     S = min(BALANCE // T, MAX_SPLIT, groups, slots(op, M, N, K, E) // T)
     return (U, T, S) if S >= 2 else (U, 0, 1)

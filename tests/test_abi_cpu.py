@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.mdg_abi_version() == 4
+    assert lib.mdg_abi_version() == 5
     for s in range(7):
         assert mdg.status_string(s)
     assert mdg.status_string(99) == "unknown status"
@@ -62,8 +62,10 @@ def test_fwd_dgrad_refusals(lib, fn):
     assert call(M=-1) == EINVAL
     assert call(N=0) == EINVAL
     assert call(E=0) == EINVAL
-    assert call(N=96) == EUNSUP        # n % 64
-    assert call(K=96) == EUNSUP        # k % 64
+    assert call(N=100) == EUNSUP       # n % 8
+    assert call(K=100) == EUNSUP       # k % 8
+    for n, k in [(96, 256), (256, 72), (8, 8), (264, 1032)]:   # multiples of 8 are sized, not refused
+        assert wsf(8, n, k, 4) > 0 and call(N=n, K=k, wsb=0) == EWS
     assert call(E=1025) == EUNSUP      # too many groups
     # pointers
     assert call(a=0) == EINVAL
@@ -172,7 +174,7 @@ def test_chunk_rows_rule(lib):
         assert r == lib.grouped_det_gemm_wgrad_chunk_rows(M, N, K, E)
     # big tiles per expert: no split at all for the 8-expert Mixtral-like shape
     assert lib.grouped_det_gemm_wgrad_chunk_rows(16384, 14336, 4096, 8) >= 16384
-    assert lib.grouped_det_gemm_wgrad_chunk_rows(8, 200, 64, 1) == 0      # invalid sizes
+    assert lib.grouped_det_gemm_wgrad_chunk_rows(8, 204, 64, 1) == 0      # invalid sizes
 
 
 @pytest.mark.parametrize("M,N,K,E", [(512, 256, 256, 4), (5000, 256, 64, 3), (65536, 2048, 7168, 256),
@@ -211,7 +213,7 @@ def test_prepare_fwd_dgrad_refuses_like_one_shot(lib, op):
     one = getattr(lib, "grouped_det_gemm_" + op)
     name = "grouped_det_gemm_prepare_" + op
     need = getattr(lib, "grouped_det_gemm_%s_workspace_bytes" % op)(8, 256, 256, 4)
-    bad = [dict(M=-1), dict(N=128), dict(K=96), dict(E=1025), dict(a=0), dict(a=A + 8),
+    bad = [dict(M=-1), dict(N=128), dict(K=100), dict(E=1025), dict(a=0), dict(a=A + 8),
            dict(ws=0), dict(wsb=need - 1), dict(ws=WS + 16), dict(d=A + 16), dict(ws=B)]
     for kw in bad:
         a = dict(a=A, w=B, o=C, d=D, M=8, N=256, K=256, E=4, ws=WS, wsb=need)

@@ -94,6 +94,13 @@ def test_tiny_indptr_form():
     ([700, 3], 64, 64, 1),                   # n = 64: a single partial tile
     ([1000, 3000], 1088, 256, 0),            # partial n tile with the wgrad row split
     ([513, 0, 1, 1400], 2880, 2880, 3),      # n = k = 2880 (11.25 tiles of 256)
+    # n and k multiples of 8 only: partial tiles 8 wide, and the last 32-deep
+    # reduction stage of fwd (over k) or dgrad (over n) holds 8, 16 or 24 columns
+    ([1, 300, 0, 40], 8, 8, 2),              # one stage of 8 columns, one partial tile
+    ([257, 0, 513], 56, 200, 1),             # dgrad stage of 24, fwd stage of 8 (fwd split)
+    ([0, 700, 33, 256], 264, 1032, 0),       # tiles of 8 in n and k; both splits end partial
+    ([1000, 3000], 48, 120, 0),              # wgrad row split; stages of 16 and 24
+    ([513, 0, 1, 1400], 2888, 80, 3),        # fwd stage of 16; dgrad split, last stage of 8
 ])
 def test_small_ragged_full(sizes, N, K, pad):
     d = make_inputs(sizes=sizes, N=N, K=K, extra_rows=pad, seed=3, device=DEV)

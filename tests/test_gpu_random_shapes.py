@@ -1,5 +1,6 @@
 """Seeded random shapes on the GPU against the oracle: expert counts 1-12, N and K
-multiples of 64 up to 1024 / 768 (partial 256-wide tiles in every direction),
+multiples of 8 up to 1024 / 768 (partial 256-wide tiles in every direction and
+reductions that end in a partial 32-deep stage),
 group sizes drawn four ways (uniform, Dirichlet-skewed, tile-boundary values,
 mostly empty), padding rows; every output element of fwd, dgrad and wgrad (bf16
 and fp32) against the fp64 oracle, and both accumulate dtypes bitwise against
@@ -19,8 +20,8 @@ DEV = "cuda:0"
 def _shape(seed):
     rng = np.random.default_rng(1000 + seed)
     E = int(rng.integers(1, 13))
-    N = 64 * int(rng.integers(1, 17))
-    K = 64 * int(rng.integers(1, 13))
+    N = 8 * int(rng.integers(1, 129))
+    K = 8 * int(rng.integers(1, 97))
     kind = seed % 4
     if kind == 0:
         sizes = rng.integers(0, 400, E)
@@ -33,7 +34,7 @@ def _shape(seed):
     return np.asarray(sizes, dtype=np.int64), N, K, int(rng.integers(0, 6))
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_shape(seed):
     sizes, N, K, pad = _shape(seed)
     label = f"seed={seed} sizes={sizes.tolist()} N={N} K={K} pad={pad}"

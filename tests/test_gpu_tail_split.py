@@ -1,5 +1,6 @@
 """The fwd/dgrad tail split on the GPU: parity with the oracle for cases with 8,
-3 or 4 pieces per tail unit and without a split, bitwise reruns, and a workspace
+3, 4 or 7 pieces per tail unit and without a split (also with a reduction that
+ends in a partial stage), bitwise reruns, and a workspace
 reused across calls of different sizes."""
 import numpy as np
 import pytest
@@ -19,6 +20,9 @@ CASES = [
     ([4352], 2048, 256, 0, {"fwd": 1, "dgrad": 8}),
     ([0, 511, 1, 0, 257], 768, 384, 9, {}),
     ([4352], 1088, 320, 2, {"fwd": 3, "dgrad": 7}),      # partial n tiles, split tail
+    # k (fwd) and n (dgrad) not multiples of 32: the last piece ends in a partial stage
+    ([300, 700], 512, 1000, 3, {"fwd": 8, "dgrad": 4}),
+    ([4352], 1032, 328, 2, {"fwd": 3, "dgrad": 7}),
 ]
 
 
