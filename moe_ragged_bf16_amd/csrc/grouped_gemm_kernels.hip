@@ -679,6 +679,12 @@ __device__ __forceinline__ void epilogue_store(const Acc& acc, const OutTile& t,
     }
 }
 
+// Cache policy of the accumulating epilogues' destination reads and writes:
+// non-temporal.  The destination is touched once per call, and without the hint
+// its lines push the operand panels other units still read out of the L2
+// (measured: fine-grained and many-expert shapes 3-6 % faster, bitwise the same).
+constexpr int kStreaming = 2;
+
 // dst = RN32(dst + acc) over the wave's fp32 sub-tile: one IEEE fp32 add per
 // element of the finished product (no contraction).  The destination reads of
 // the next half slab are in flight while the current one is staged and added.
@@ -687,7 +693,7 @@ __device__ __forceinline__ void epilogue_accumulate(const Acc& acc, const OutTil
   const Staging x = staging(xb, lane, false);
   f32x4 old[2][8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, 0);
+  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, kStreaming);
 #pragma unroll
   for (int hs = 0; hs < 8; ++hs) {
     const int ib = hs >> 1, jh = hs & 1;
@@ -695,7 +701,7 @@ __device__ __forceinline__ void epilogue_accumulate(const Acc& acc, const OutTil
     if (hs + 1 < 8) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        old[(hs + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, (hs + 1) >> 1, q, (hs + 1) & 1), 0, 0);
+        old[(hs + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, (hs + 1) >> 1, q, (hs + 1) & 1), 0, kStreaming);
     }
     stage_slab<kStoreF32>(acc, x, ib, jh);
     u32x4 v[8];
@@ -708,7 +714,7 @@ __device__ __forceinline__ void epilogue_accumulate(const Acc& acc, const OutTil
       o[1] = __fadd_rn(o[1], n[1]);
       o[2] = __fadd_rn(o[2], n[2]);
       o[3] = __fadd_rn(o[3], n[3]);
-      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, jh), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, jh), 0, kStreaming);
     }
   }
 }
@@ -723,14 +729,14 @@ __device__ __forceinline__ void epilogue_accumulate_bf16(const Acc& acc, const O
   const Staging x = staging(xb, lane, true);
   u32x4 old[2][8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, 0);
+  for (int q = 0; q < 8; ++q) old[0][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, 0, q, 0), 0, kStreaming);
 #pragma unroll
   for (int ib = 0; ib < 4; ++ib) {
     __builtin_amdgcn_sched_barrier(0);  // one slab at a time (bounds the registers in use)
     if (ib + 1 < 4) {
 #pragma unroll
       for (int q = 0; q < 8; ++q)
-        old[(ib + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, ib + 1, q, 0), 0, 0);
+        old[(ib + 1) & 1][q] = __builtin_amdgcn_raw_buffer_load_b128(t.rs, slab_off(t, ib + 1, q, 0), 0, kStreaming);
     }
     stage_slab<kStoreBf16>(acc, x, ib, 0);
     u32x4 v[8];
@@ -740,7 +746,7 @@ __device__ __forceinline__ void epilogue_accumulate_bf16(const Acc& acc, const O
       u32x4 o = old[ib & 1][q];
 #pragma unroll
       for (int c = 0; c < 4; ++c) o[c] = add_bf16x2(o[c], v[q][c]);
-      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, 0), 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, t.rs, slab_off(t, ib, q, 0), 0, kStreaming);
     }
   }
 }
@@ -952,6 +958,15 @@ struct Pipe {
   // operands with the reduction strided: W in dgrad, G and X in wgrad
   static constexpr bool ATC = (OP == kWgrad);
   static constexpr bool BTC = (OP != kFwd);
+  // Stages loaded in pairs (fwd, dgrad: an operand is read along its rows).  A
+  // stage of such an operand holds 64 bytes of each row, half a 128-byte cache
+  // line, and the next stage the other half: loaded a step apart, every line
+  // would come from the L2 twice (the L1 no longer holds it); requested by
+  // consecutive instructions, the L1 merges the two halves into one fetch.
+  // (Transposed operands load 512-byte row segments, whole lines already, so
+  // dgrad pairs only A; wgrad pairs nothing.)
+  static constexpr bool kPairs = !(ATC && BTC);
+  static constexpr bool kPairB = kPairs && !BTC;
   uint32_t off_a[4], off_b[4];
   uint32_t cb_a[4], cb_b[4];  // MASK: chunk byte positions of the RC loads (dma_chunks_rc)
   int w, wi, wj, lane;
@@ -968,16 +983,71 @@ struct Pipe {
     else dma_stage<BTC>(x.b, off_b, stage_b<S>() + w * 1024, kt, kt < x.nk);
   }
 
-  // Stages 0..2 of a unit into buffers 0..2, and operand A of stage 3.
-  __device__ __forceinline__ void prefetch(const Unit& x) const {
-    issue_a<0>(x, 0);
-    issue_b<0>(x, 0);
-    issue_a<1>(x, 1);
-    issue_b<1>(x, 1);
+  // One load of stage kt's operand (masked when the stage may be partial).
+  template <bool TC>
+  __device__ __forceinline__ void dma_q(const DmaStage& d, uint32_t off, uint32_t cb, uint32_t kv, int q) const {
+    if constexpr (MASK && !TC) dma_one_masked(d, off, cb, kv, q);
+    else dma_one(d, off, q);
+  }
+
+  // This wave's loads of operand A (resp. B) of stages kt and kt+1 into buffers
+  // S and S+1, the two halves of each row segment by consecutive instructions.
+  template <int S>
+  __device__ __forceinline__ void issue_a_pair(const Unit& x, int kt) const {
+    const DmaStage d0 = dma_begin<ATC>(x.a, stage_a<S>() + w * 1024, kt, kt < x.nk);
+    const DmaStage d1 = dma_begin<ATC>(x.a, stage_a<S + 1>() + w * 1024, kt + 1, kt + 1 < x.nk);
+    const uint32_t k0 = MASK && !ATC ? stage_valid_bytes(x.a, kt) : 0;
+    const uint32_t k1 = MASK && !ATC ? stage_valid_bytes(x.a, kt + 1) : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma_q<ATC>(d0, off_a[q], cb_a[q], k0, q);
+      dma_q<ATC>(d1, off_a[q], cb_a[q], k1, q);
+    }
+  }
+  template <int S>
+  __device__ __forceinline__ void issue_b_pair(const Unit& x, int kt) const {
+    const DmaStage d0 = dma_begin<BTC>(x.b, stage_b<S>() + w * 1024, kt, kt < x.nk);
+    const DmaStage d1 = dma_begin<BTC>(x.b, stage_b<S + 1>() + w * 1024, kt + 1, kt + 1 < x.nk);
+    const uint32_t k0 = MASK && !BTC ? stage_valid_bytes(x.b, kt) : 0;
+    const uint32_t k1 = MASK && !BTC ? stage_valid_bytes(x.b, kt + 1) : 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      dma_q<BTC>(d0, off_b[q], cb_b[q], k0, q);
+      dma_q<BTC>(d1, off_b[q], cb_b[q], k1, q);
+    }
+  }
+
+  // A unit's first stages, loaded while the previous unit's epilogue runs (or
+  // at the start): stages 0..2, and operand A of stage 3 (kPairs: stages 0 and
+  // 1 as a pair, then stage 2).  The rest of stage 3 follows the epilogue
+  // (issue_last), whose staging buffers are stage 3's.
+  __device__ __forceinline__ void prefetch_first(const Unit& x) const {
+    if constexpr (kPairB) {
+      issue_a_pair<0>(x, 0);
+      issue_b_pair<0>(x, 0);
+    } else if constexpr (kPairs) {
+      issue_a_pair<0>(x, 0);
+      issue_b<0>(x, 0);
+      issue_b<1>(x, 1);
+    } else {
+      issue_a<0>(x, 0);
+      issue_b<0>(x, 0);
+      issue_a<1>(x, 1);
+      issue_b<1>(x, 1);
+    }
     issue_a<2>(x, 2);
     issue_b<2>(x, 2);
-    issue_a<3>(x, 3);
   }
+  __device__ __forceinline__ void issue_last(const Unit& x) const {
+    issue_a<3>(x, 3);
+    if constexpr (kPairB) issue_b<3>(x, 3);  // (otherwise the first step issues it)
+  }
+  // Loads issued after the last one of what a unit's first step needs (fwd:
+  // the pairs of stages 0, 1, followed by stage 2 and stage 3; dgrad: B of
+  // stage 0, followed by B of stage 1, stage 2 and A of stage 3; wgrad: B of
+  // stage 0, followed by stages 1, 2 and A of stage 3), up to and including
+  // issue_last, not counting the epilogue's own operations in between.
+  static constexpr int kAfterStage0 = kPairs ? 2 * kDmaPerStage : 2 * kDmaPerStage + kDmaPerStage / 2;
 
   // Stage kt, held in buffer S = kt % 4.  On entry its 8 B fragments are in fbc
   // and its A fragments of row blocks 0..3 in fal.  First half: read the A
@@ -1004,6 +1074,10 @@ struct Pipe {
   __device__ __forceinline__ void step(Acc& acc, const bf16x8 (&fbc)[8], bf16x8 (&fbn)[8],
                                        bf16x8 (&fal)[4], bf16x8 (&fah)[4], const Unit& x, int kt, int& e1,
                                        int& e2) const {
+    if constexpr (kPairs) {
+      step_pairs<S, kFirst>(acc, fbc, fbn, fal, fah, x, kt, e1);
+      return;
+    }
     constexpr int S1 = (S + 1) & 3, S3 = (S + 3) & 3;
     static_assert(kDmaPerStage == 8, "4 loads per operand and wave");
     // first half: row blocks 0..3; reads of fah early, operand B of stage kt+3
@@ -1052,6 +1126,112 @@ struct Pipe {
   }
 
   // Stage 0's B fragments and A fragments of row blocks 0..3 (after its wait).
+  // The step with stages in pairs (kPairs).  Operand A of stages 2m and 2m+1
+  // is issued in the second half of step 2m-3 (odd), into the buffers of
+  // stages 2m-4 and 2m-3, which no wave reads any more once every wave is past
+  // step 2m-3's first half.  Two loads per column block there, 8 per half step
+  // at most, because a burst of loads in one half stalls the MFMAs behind them.
+  //
+  // fwd (kPairB): operand B of stages 2m, 2m+1 follows in the first half of
+  // step 2m-2 (even).  Only odd steps synchronise: they wait for the pair their
+  // second half starts reading (nothing is issued after it by then, so the
+  // wait is for all of this wave's loads) and pass one barrier, which makes the
+  // pair visible everywhere and frees the buffers the next A and B pairs go to
+  // (B's even-step loads go to buffers last read before that barrier).  An even
+  // step reads the second stage of a pair waited for one step earlier.
+  //
+  // dgrad: operand B (transposed, whole lines) keeps its per-stage slot, the
+  // first half of step kt-3 for stage kt, and every step waits and passes the
+  // barrier.  The wait for stage kt+1 allows the loads issued after its last
+  // one: for even kt, B of stage kt+1 is last and 16 follow (B of kt+2, the A
+  // pair of kt+3 and kt+4, B of kt+3); for odd kt, A of stage kt+1 is last but
+  // one in its pair and 9 follow (A of kt+2's last load, B of kt+2 and kt+3).
+  // A unit's first two steps also count the loads of the prologue and the
+  // previous unit's epilogue (e1): step 0 waits for B of stage 1 (followed by
+  // stage 2, e1, A and B of stage 3: 16 + e1); step 1 for B of stage 2
+  // (followed by e1, A of stage 3, B of stages 3 and 4: 12 + e1).
+  template <int S, bool kFirst>
+  __device__ __forceinline__ void step_pairs(Acc& acc, const bf16x8 (&fbc)[8], bf16x8 (&fbn)[8],
+                                             bf16x8 (&fal)[4], bf16x8 (&fah)[4], const Unit& x, int kt,
+                                             int e1) const {
+    constexpr int S1 = (S + 1) & 3, S2 = (S + 2) & 3, S3 = (S + 3) & 3;
+    constexpr bool kOdd = (S & 1) != 0;
+    // first half: B loads (fwd: the pair kt+2, kt+3 on even steps but the first,
+    // whose stages 2 and 3 came with the prologue; dgrad: stage kt+3)
+    constexpr bool kIssueB = kPairB ? (!kOdd && !(kFirst && S == 0)) : true;
+    DmaStage b0{}, b1{};
+    uint32_t kb0 = 0, kb1 = 0;
+    if constexpr (kIssueB) {
+      if constexpr (kPairB) {
+        b0 = dma_begin<BTC>(x.b, stage_b<S2>() + w * 1024, kt + 2, kt + 2 < x.nk);
+        b1 = dma_begin<BTC>(x.b, stage_b<S3>() + w * 1024, kt + 3, kt + 3 < x.nk);
+        if constexpr (MASK) {
+          kb0 = stage_valid_bytes(x.b, kt + 2);
+          kb1 = stage_valid_bytes(x.b, kt + 3);
+        }
+      } else {
+        b0 = dma_begin<BTC>(x.b, stage_b<S3>() + w * 1024, kt + 3, kt + 3 < x.nk);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      mma_col(acc, fbc[jb], fal, 0, jb);
+      if (jb < 4) fah[jb] = load_frag<ATC>(stage_a<S>(), wi * 128 + 64 + 16 * jb, lane);
+      if constexpr (kIssueB) {
+        const int q = jb >> 1;
+        if constexpr (kPairB) {
+          if ((jb & 1) == 0) {
+            dma_q<BTC>(b0, off_b[q], cb_b[q], kb0, q);
+            dma_q<BTC>(b1, off_b[q], cb_b[q], kb1, q);
+          }
+        } else if (jb & 1) {
+          dma_q<BTC>(b0, off_b[q], cb_b[q], 0, q);
+        }
+      }
+    }
+    if constexpr (kPairB) {
+      if constexpr (kOdd) wait_vm_lgkm<0>();  // stages kt+1, kt+2 have landed; stage kt's reads returned
+    } else if constexpr (kFirst && S == 0) {
+      wait_vm(2 * kDmaPerStage + e1);
+    } else if constexpr (kFirst && S == 1) {
+      wait_vm(kDmaPerStage + kDmaPerStage / 2 + e1);
+    } else {
+      wait_vm_lgkm<kOdd ? kDmaPerStage + 1 : 2 * kDmaPerStage>();  // stage kt+1 has landed
+    }
+    if constexpr (!kPairB || kOdd) lds_barrier();  // ... in every wave; stage kt's reads returned
+    // second half: operand A of stages kt+3, kt+4 on odd steps
+    DmaStage a0{}, a1{};
+    uint32_t ka0 = 0, ka1 = 0;
+    if constexpr (kOdd) {
+      a0 = dma_begin<ATC>(x.a, stage_a<S3>() + w * 1024, kt + 3, kt + 3 < x.nk);
+      a1 = dma_begin<ATC>(x.a, stage_a<S>() + w * 1024, kt + 4, kt + 4 < x.nk);
+      if constexpr (MASK) {
+        ka0 = stage_valid_bytes(x.a, kt + 3);
+        ka1 = stage_valid_bytes(x.a, kt + 4);
+      }
+    }
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) {
+      mma_col(acc, fbc[jb], fah, 4, jb);
+      if (jb == 0) {
+        fbn[0] = load_frag<BTC>(stage_b<S1>(), wj * 128, lane);
+        fal[0] = load_frag<ATC>(stage_a<S1>(), wi * 128, lane);
+      } else if (jb < 4) {
+        fal[jb] = load_frag<ATC>(stage_a<S1>(), wi * 128 + 16 * jb, lane);
+        fbn[jb] = load_frag<BTC>(stage_b<S1>(), wj * 128 + 16 * jb, lane);
+      } else {
+        fbn[jb] = load_frag<BTC>(stage_b<S1>(), wj * 128 + 16 * jb, lane);
+      }
+      if constexpr (kOdd) {
+        const int q = jb >> 1;
+        if ((jb & 1) == 0) {
+          dma_q<ATC>(a0, off_a[q], cb_a[q], ka0, q);
+          dma_q<ATC>(a1, off_a[q], cb_a[q], ka1, q);
+        }
+      }
+    }
+  }
+
   __device__ __forceinline__ void first_frags(bf16x8 (&fb)[8], bf16x8 (&fal)[4]) const {
     fb[0] = load_frag<BTC>(stage_b<0>(), wj * 128, lane);
 #pragma unroll
@@ -1142,7 +1322,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   }
 
   Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
-  if (cur.valid) pipe.prefetch(cur);
+  if (cur.valid) {
+    pipe.prefetch_first(cur);
+    pipe.issue_last(cur);
+  }
   int tail = 0;  // memory operations issued between stage 2 and stage 3's operand A of the current unit
   for (int u = vb; cur.valid; u += P) {
     Acc acc;
@@ -1157,7 +1340,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     if (cur.nk > 0) {
       bf16x8 fbA[8], fbB[8], fal[4], fah[4];
       int e1 = tail, e2 = 0;
-      wait_vm(2 * kDmaPerStage + kDmaPerStage / 2 + tail);  // stage 0 has landed
+      wait_vm(Pipe<OP, MASK>::kAfterStage0 + tail);  // stage 0 (kPairs: stages 0, 1) has landed
       lds_barrier();                     // ... in every wave
       pipe.first_frags(fbA, fal);
       // nk is a positive multiple of 4: the first 4 steps, then the steady state
@@ -1193,14 +1376,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // (the last stage buffers, 8 KiB per wave) to memory; operand A of stage 3
     // follows once every wave is done with them.
     const Unit nxt = decode_item<OP>(p, tb, us, total, pl, u + P);
-    if (nxt.valid) {
-      pipe.template issue_a<0>(nxt, 0);
-      pipe.template issue_b<0>(nxt, 0);
-      pipe.template issue_a<1>(nxt, 1);
-      pipe.template issue_b<1>(nxt, 1);
-      pipe.template issue_a<2>(nxt, 2);
-      pipe.template issue_b<2>(nxt, 2);
-    }
+    if (nxt.valid) pipe.prefetch_first(nxt);
     const int ln = lane_here();
     const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, ln,
                                 is_bf16_mode(cur.mode) ? 2 : 4);
@@ -1212,7 +1388,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     else tail = run_epilogue<OP, OUT>(acc, cur, ot, s_b3 + (pipe.w & 1) * 8192, ln, rmw);
     wait_vm_lgkm<63>();  // the staging reads have returned ...
     lds_barrier();       // ... in every wave
-    if (nxt.valid) pipe.template issue_a<3>(nxt, 3);
+    if (nxt.valid) pipe.issue_last(nxt);
     cur = nxt;
   }
   wait_vm_lgkm<0>();
