@@ -16,6 +16,7 @@ constexpr int kStages = 4;       // LDS stages (kStages - 1 in flight)
 constexpr int kKAlign = 8;       // k must be a multiple of this: rows of whole 16-byte chunks
 constexpr int kNAlign = 8;       // n likewise (partial tiles and partial reduction stages are masked)
 constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
+constexpr int kPairRows = 2048;  // fwd loads stages in pairs when m_rows >= kPairRows * num_groups
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
 constexpr int64_t kMaxRows = 4000000;  // m_rows limit (row indices and group sizes stay well inside int32)

@@ -953,7 +953,8 @@ __device__ __forceinline__ uint8_t* stage_b() {
 
 // MASK: the reduction extent is not a multiple of 32, so the last stage of an
 // RC operand is partial and its loads mask the chunks past the extent.
-template <int OP, bool MASK>
+// PAIRS: stages of the row-read operands are loaded in pairs (see kPairs).
+template <int OP, bool MASK, bool PAIRS>
 struct Pipe {
   // operands with the reduction strided: W in dgrad, G and X in wgrad
   static constexpr bool ATC = (OP == kWgrad);
@@ -964,8 +965,11 @@ struct Pipe {
   // would come from the L2 twice (the L1 no longer holds it); requested by
   // consecutive instructions, the L1 merges the two halves into one fetch.
   // (Transposed operands load 512-byte row segments, whole lines already, so
-  // dgrad pairs only A; wgrad pairs nothing.)
-  static constexpr bool kPairs = !(ATC && BTC);
+  // dgrad pairs only A; wgrad pairs nothing.)  The pairing shortens by one
+  // step the lead of the first stage of each pair, which costs more than it
+  // saves when a unit streams its weights from HBM (few rows per expert), so
+  // for fwd it is a launch choice.
+  static constexpr bool kPairs = PAIRS && !(ATC && BTC);
   static constexpr bool kPairB = kPairs && !BTC;
   uint32_t off_a[4], off_b[4];
   uint32_t cb_a[4], cb_b[4];  // MASK: chunk byte positions of the RC loads (dma_chunks_rc)
@@ -1284,10 +1288,11 @@ __device__ __forceinline__ int run_epilogue(const Acc& acc, const Unit& cur, con
 // OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or their
 // accumulating forms for wgrad).  Units of split wgrad experts store fp32
 // partials.
-template <int OP, int OUT, bool MASK>
+template <int OP, int OUT, bool MASK, bool PAIRS>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p) {
-  constexpr bool ATC = Pipe<OP, MASK>::ATC;
-  constexpr bool BTC = Pipe<OP, MASK>::BTC;
+  using Pp = Pipe<OP, MASK, PAIRS>;
+  constexpr bool ATC = Pp::ATC;
+  constexpr bool BTC = Pp::BTC;
   __shared__ int s_end[kMaxGroups];
   __shared__ int s_uprefix[kMaxGroups + 1];
   __shared__ int s_sprefix[kMaxGroups];
@@ -1306,7 +1311,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
   const int bid = blockIdx.x;
   const int vb = (P % 8 == 0) ? (bid % 8) * (P / 8) + bid / 8 : bid;
 
-  Pipe<OP, MASK> pipe;
+  Pp pipe;
   pipe.lane = threadIdx.x & 63;
   pipe.w = uniform(threadIdx.x >> 6);
   pipe.wi = pipe.w >> 1;
@@ -1340,7 +1345,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     if (cur.nk > 0) {
       bf16x8 fbA[8], fbB[8], fal[4], fah[4];
       int e1 = tail, e2 = 0;
-      wait_vm(Pipe<OP, MASK>::kAfterStage0 + tail);  // stage 0 (kPairs: stages 0, 1) has landed
+      wait_vm(Pp::kAfterStage0 + tail);  // stage 0 (kPairs: stages 0, 1) has landed
       lds_barrier();                     // ... in every wave
       pipe.first_frags(fbA, fal);
       // nk is a positive multiple of 4: the first 4 steps, then the steady state
@@ -1540,23 +1545,32 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(kThreads);
   switch (op) {
-    case kFwd:  // the reduction is k
-      if (p.k % kTileR == 0) hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, false>), g, blk, 0, stream, p);
-      else hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, true>), g, blk, 0, stream, p);
+    case kFwd: {  // the reduction is k
+      // paired stages when the experts average at least kPairRows rows (W reused
+      // from the L2 by several row tiles); measured as the better schedule there
+      const bool pairs = p.m_rows >= (int64_t)kPairRows * p.num_groups;
+      if (p.k % kTileR == 0) {
+        if (pairs) hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, false, true>), g, blk, 0, stream, p);
+        else hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, false, false>), g, blk, 0, stream, p);
+      } else {
+        if (pairs) hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, true, true>), g, blk, 0, stream, p);
+        else hipLaunchKernelGGL((grouped_gemm_kernel<kFwd, kStoreBf16, true, false>), g, blk, 0, stream, p);
+      }
       break;
+    }
     case kDgrad:  // the reduction is n
-      if (p.n % kTileR == 0) hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, false>), g, blk, 0, stream, p);
-      else hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, true>), g, blk, 0, stream, p);
+      if (p.n % kTileR == 0) hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, false, true>), g, blk, 0, stream, p);
+      else hipLaunchKernelGGL((grouped_gemm_kernel<kDgrad, kStoreBf16, true, true>), g, blk, 0, stream, p);
       break;
     case kWgrad:
       if (!p.out_fp32 && !p.accumulate)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16, false>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16, false, false>), g, blk, 0, stream, p);
       else if (!p.out_fp32)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16Acc, false>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreBf16Acc, false, false>), g, blk, 0, stream, p);
       else if (!p.accumulate)
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32, false>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32, false, false>), g, blk, 0, stream, p);
       else
-        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc, false>), g, blk, 0, stream, p);
+        hipLaunchKernelGGL((grouped_gemm_kernel<kWgrad, kStoreF32Acc, false, false>), g, blk, 0, stream, p);
       break;
   }
   return hipGetLastError();

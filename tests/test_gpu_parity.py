@@ -230,3 +230,23 @@ def test_max_group_count(E):
     d = make_inputs(sizes=sizes, N=256, K=128, extra_rows=3, seed=E, device=DEV)
     print(f"E={E} rows={int(sizes.sum())}", flush=True)
     _check_full(d, f"E={E}")
+
+
+@pytest.mark.parametrize("K", [320, 328])
+def test_fwd_schedules_agree(K):
+    """fwd loads stages in pairs when the rows average at least 2048 per expert
+    and one by one otherwise (a launch choice from m_rows and the group count);
+    padding rows past the last group switch it without changing any group, and
+    both schedules sum in the same order, so the outputs agree bit for bit.  K =
+    328 also runs the masked last stage under both."""
+    sizes = [700, 300, 1100]
+    d = make_inputs(sizes=sizes, N=512, K=K, extra_rows=3 * 2048 - 2100, seed=51, device=DEV)
+    t = int(np.sum(sizes))
+    assert d["M"] >= 2048 * 3                       # paired schedule
+    y_pairs = mdg.grouped_det_gemm_fwd(d["x"], d["w"], d["offs"])
+    y_single = mdg.grouped_det_gemm_fwd(d["x"][:t].contiguous(), d["w"], d["offs"])   # M = t < 2048 * 3
+    torch.cuda.synchronize()
+    assert torch.equal(y_pairs[:t].view(torch.int16), y_single.view(torch.int16))
+    X, W = bits(d["x"][:t]), bits(d["w"])
+    e = group_errs(values(y_single), oracle.fwd(X, W, d["offs"].cpu().numpy())[:t], np.array(sizes))
+    assert max(e) <= TOL_BF16
