@@ -1053,6 +1053,8 @@ struct Pipe {
   // issue_last, not counting the epilogue's own operations in between.
   static constexpr int kAfterStage0 = kPairs ? 2 * kDmaPerStage : 2 * kDmaPerStage + kDmaPerStage / 2;
 
+  // The per-stage step (wgrad; fwd and dgrad load stages in pairs, see
+  // step_pairs, which keeps the same MFMA and fragment-read order).
   // Stage kt, held in buffer S = kt % 4.  On entry its 8 B fragments are in fbc
   // and its A fragments of row blocks 0..3 in fal.  First half: read the A
   // fragments of row blocks 4..7 into fah, issue operand B of stage kt+3 (zeros
