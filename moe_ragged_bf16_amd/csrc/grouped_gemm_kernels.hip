@@ -24,9 +24,12 @@
 //    after whole rounds into reduction ranges (the tail split below).
 //  * The reduction is staged 32 deep into a ring of 4 LDS buffers per operand
 //    by buffer loads that write LDS directly (no registers); the buffer range
-//    check turns rows past a group's or chunk's end into zeros.  Three stages
-//    are in flight while the MFMAs of the current one run; the next unit's
-//    first stages load during the current epilogue.
+//    check turns rows past a group's or chunk's end into zeros.  Up to three
+//    stages are in flight while the MFMAs of the current one run; the next
+//    unit's first stages load during the current epilogue.  Where an operand is
+//    read along its rows (fwd; dgrad's A), two consecutive stages hold the two
+//    halves of each 128-byte line and are loaded as a pair, so that the L1
+//    fetches every line from the L2 once (see Pipe::kPairs).
 //  * LDS layouts follow the memory layout of each operand, with 16-byte-chunk
 //    XOR swizzles that keep the fragment reads free of bank conflicts:
 //      r-contiguous operand  [256 rows][32 r]  read with ds_read_b128;
