@@ -1331,6 +1331,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     dma_chunks_rc(pipe.cb_b, pipe.w, pipe.lane);
   }
 
+  // wgrad: every unit ends in a long epilogue (the main_grad read-modify-write)
+  // and the units of a persistent launch start together, so the first
+  // epilogues of all workgroups coincide and contend for HBM (measured: unit 0's
+  // take ~20 us on all CUs at once, ~10 us once they have drifted apart).
+  // Half of each XCD's workgroups start ~16k cycles later, which spreads them
+  // from the first unit on (+1 to +2 % on the Mixtral-like, gate_up and fine
+  // shapes; bitwise the same).  Not worth it for launches of a few units.
+  if (OP == kWgrad && ((bid >> 3) & 1) && total >= 4 * P) {
+#pragma unroll 1
+    for (int i = 0; i < 2; ++i) __builtin_amdgcn_s_sleep(127);
+  }
   Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
   if (cur.valid) {
     pipe.prefetch_first(cur);
