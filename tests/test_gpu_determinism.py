@@ -185,3 +185,40 @@ def test_inference_tensors():
     assert torch.equal(mg.view(torch.int32), mg0.view(torch.int32))
     assert torch.equal(dx[:1000].view(torch.int16),
                        mdg.grouped_det_gemm_dgrad(d["g"], d["w"], d["offs"])[:1000].view(torch.int16))
+
+
+@pytest.mark.parametrize("bad", [
+    [-5, 700, 300, 5000, 2000],      # negative, decreasing, past m_rows
+    [2**31 - 1] * 5,                 # all past m_rows: group 0 takes every row
+    [-2**31, -1, 0, -7, 2900],       # negatives
+])
+def test_malformed_offsets_act_as_clamped(bad):
+    """The kernels clamp each offset to [0, m_rows] and take the running maximum, so a
+    malformed array reads and writes nothing out of bounds and gives, bit for bit, the
+    result of its sanitised form (every host-side size depends on m_rows and the group
+    count only, which any sanitised array respects)."""
+    M, N, K = 3000, 520, 328
+    d = make_inputs(sizes=[600] * 5, N=N, K=K, seed=21, device=DEV, tensors=("x", "w", "g", "main_grad"))
+    clean = np.maximum.accumulate(np.clip(np.asarray(bad, dtype=np.int64), 0, M))
+
+    def run(offs):
+        y = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=DEV)
+        dx = torch.full((M, K), 7.0, dtype=torch.bfloat16, device=DEV)
+        mdg.grouped_det_gemm_fwd(d["x"], d["w"], offs, out=y)
+        mdg.grouped_det_gemm_dgrad(d["g"], d["w"], offs, out=dx)
+        dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], offs, out_dtype=torch.float32)
+        mg = d["main_grad"].clone()
+        mdg.grouped_det_gemm_wgrad(d["g"], d["x"], offs, out=mg, accumulate=True)
+        torch.cuda.synchronize()
+        return [y.view(torch.int16), dx.view(torch.int16), dw.view(torch.int32), mg.view(torch.int32)]
+
+    got = run(torch.tensor(bad, dtype=torch.int32, device=DEV))
+    want = run(torch.tensor(clean, dtype=torch.int32, device=DEV))
+    for a, b in zip(got, want):
+        assert torch.equal(a, b)
+    # the sanitised groups: empty ones give exactly zero dW, rows past the last end stay untouched
+    sizes = np.diff(np.concatenate([[0], clean]))
+    for e in np.flatnonzero(sizes == 0):
+        assert torch.all(got[2][e] == 0)
+    if clean[-1] < M:
+        assert torch.all(got[0][clean[-1]:] == torch.tensor(7.0, dtype=torch.bfloat16).view(torch.int16).item())
