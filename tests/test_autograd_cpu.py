@@ -152,6 +152,7 @@ def test_create_graph_refused(case, fuse):
         torch.autograd.grad(y, [case["x"], w], case["dy"], create_graph=True)
 
 
+@pytest.mark.filterwarnings("ignore:`torch.jit.trace` is deprecated:DeprecationWarning")
 def test_trace_refused(case):
     with pytest.raises(NotImplementedError):
         torch.jit.trace(lambda a, b: cake_grouped_det_mm(a, b, case["offs"]), (case["x"], case["w"]))
