@@ -31,9 +31,10 @@
  *  - Groups.  offs holds num_groups int32 cumulative END offsets, on the device;
  *    the host never reads it.  A caller holding m_indptr[E + 1] (leading zero)
  *    passes m_indptr + 1.  Offsets must be non-decreasing and within
- *    [0, m_rows]; the kernels clamp them, so bad offsets never access memory out
- *    of bounds, but the results are then unspecified.  Rows at or past
- *    offs[E-1] belong to no group: fwd and dgrad leave those output rows
+ *    [0, m_rows].  An array that breaks this still accesses no memory out of
+ *    bounds: the kernels use end[e] = max over e' <= e of
+ *    min(max(offs[e'], 0), m_rows), so it gives the results of that sanitised
+ *    array.  Rows at or past end[E-1] belong to no group: fwd and dgrad leave those output rows
  *    untouched and wgrad ignores them.
  *  - Shapes.  1 <= num_groups <= 1024, m_rows >= 0, n >= 8 with n % 8 == 0,
  *    k >= 8 with k % 8 == 0.  (The API page states n % 256 == 0 and k % 64 == 0
@@ -173,15 +174,17 @@ int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
 
 /*
  * Zero fill of the rows that belong to no group: out[r, :] = 0 for
- * offs[num_groups-1] <= r < m_rows (Cake ragged BF16 grouped GEMM API page,
+ * end <= r < m_rows (Cake ragged BF16 grouped GEMM API page,
  * introduction: groups are consecutive row ranges ending at offs[E-1]; the row
  * padding case of flashinfer PR #8924, "Tests").  fwd and dgrad leave those
  * rows untouched; an autograd wrapper uses this to give them a defined value
  * (zero: they depend on no input) without the host reading offs.
  *   out [m_rows, row_bytes] bytes, row-major, 16-byte aligned; row_bytes a
  *     positive multiple of 16 (at most 2^24).  Written only in the rows named.
- *   offs [num_groups] int32 on the device; only offs[num_groups-1] is read,
- *     clamped to [0, m_rows].  An m_indptr caller passes m_indptr + 1.
+ *   offs [num_groups] int32 on the device.  end is the last group end the
+ *     GEMM entry points use: the maximum of the offsets clamped to [0, m_rows],
+ *     i.e. offs[num_groups-1] for a valid array.  An m_indptr caller passes
+ *     m_indptr + 1.
  * m_rows == 0 enqueues nothing.  out must not overlap offs.
  */
 int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,

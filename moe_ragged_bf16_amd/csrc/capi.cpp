@@ -467,7 +467,7 @@ int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_row
   const int64_t vecs = m_rows * (row_bytes / 16);
   const int64_t cap = 2 * (int64_t)(dev.cus > 0 ? dev.cus : 256);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cap, (vecs + kThreads - 1) / kThreads));
-  if (launch_zero_rows(out, offs + (num_groups - 1), m_rows, row_bytes, grid, static_cast<hipStream_t>(stream)) !=
+  if (launch_zero_rows(out, offs, num_groups, m_rows, row_bytes, grid, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return MDG_EHIP;
   return MDG_OK;

@@ -55,8 +55,8 @@ static_assert(sizeof(TailUnit) == 24, "tail table entry");
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream);
 hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
-hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, int64_t row_bytes, int grid,
-                            hipStream_t stream);
+hipError_t launch_zero_rows(void* out, const int32_t* offs, int num_groups, int64_t m_rows, int64_t row_bytes,
+                            int grid, hipStream_t stream);
 
 // Host-side sizing helpers (capi.cpp).
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);

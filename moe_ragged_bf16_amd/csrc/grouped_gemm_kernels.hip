@@ -1540,15 +1540,24 @@ __global__ __launch_bounds__(kThreads) void tail_reduce_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // rows that belong to no group
 // ---------------------------------------------------------------------------
-// Writes zeros over rows t .. m_rows-1 of a [m_rows, row_bytes] output, with t
-// = offs[E-1] read on the device and clamped to [0, m_rows].  16 bytes per
-// thread and iteration over a grid-stride loop; with no such rows every
-// workgroup exits after one load.
-__global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const int32_t* last_end,
+// Writes zeros over rows t .. m_rows-1 of a [m_rows, row_bytes] output, where t
+// is the last group end the GEMM kernels use: the maximum of the offsets
+// clamped to [0, m_rows] (offs[E-1] itself for a valid array), found by each
+// workgroup from the E offsets.  16 bytes per thread and iteration over a
+// grid-stride loop; with no such rows every workgroup exits after the offsets.
+__global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const int32_t* offs, int num_groups,
                                                              int64_t m_rows, int64_t row_bytes) {
-  int64_t t = *last_end;
-  t = t < 0 ? 0 : (t > m_rows ? m_rows : t);
-  const int64_t begin = t * row_bytes / 16, end = m_rows * row_bytes / 16;
+  __shared__ int s_max[kThreads / 64];
+  const int M = (int)m_rows;
+  int v = 0;
+  for (int e = threadIdx.x; e < num_groups; e += kThreads) v = max(v, min(max(offs[e], 0), M));
+  v = wave_incl_max(v);
+  if ((threadIdx.x & 63) == 63) s_max[threadIdx.x >> 6] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) t = max(t, s_max[i]);
+  const int64_t begin = (int64_t)t * row_bytes / 16, end = m_rows * row_bytes / 16;
   u32x4* dst = reinterpret_cast<u32x4*>(out);
   const u32x4 z = {0u, 0u, 0u, 0u};
   for (int64_t i = begin + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < end;
@@ -1592,10 +1601,10 @@ hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream)
   return hipGetLastError();
 }
 
-hipError_t launch_zero_rows(void* out, const int32_t* last_end, int64_t m_rows, int64_t row_bytes, int grid,
-                            hipStream_t stream) {
-  hipLaunchKernelGGL(zero_rows_kernel, dim3(grid), dim3(kThreads), 0, stream, static_cast<uint8_t*>(out),
-                     last_end, m_rows, row_bytes);
+hipError_t launch_zero_rows(void* out, const int32_t* offs, int num_groups, int64_t m_rows, int64_t row_bytes,
+                            int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_rows_kernel, dim3(grid), dim3(kThreads), 0, stream, static_cast<uint8_t*>(out), offs,
+                     num_groups, m_rows, row_bytes);
   return hipGetLastError();
 }
 

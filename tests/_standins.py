@@ -66,8 +66,9 @@ class StandIns:
 
     def zero_pad_rows(self, out, offs, num_groups):
         self.calls.append("zero_pad_rows")
-        t = int(_offs(offs, num_groups)[-1])
-        out[min(max(t, 0), out.shape[0]):] = 0
+        # the last group end the kernels use: the largest offset clamped to [0, M]
+        t = int(np.clip(_offs(offs, num_groups), 0, out.shape[0]).max())
+        out[t:] = 0
         return out
 
 

@@ -152,11 +152,11 @@ def test_zero_pad_rows(dtype, cols):
         before = out.clone()
         offs = torch.tensor(ends, dtype=torch.int32, device=DEV)
         mdg.zero_pad_rows(out, offs, E)
-        t = min(max(ends[-1], 0), M)
+        t = min(max(max(ends), 0), M)   # the last end the GEMMs use: the largest clamped offset
         torch.cuda.synchronize()
         assert torch.equal(out[:t], before[:t]), ends
         assert torch.all(out[t:] == 0) and not torch.signbit(out[t:].float()).any(), ends
-    # the m_indptr form reads the same last end
+    # the m_indptr form gives the same last end
     out = torch.ones((M, cols), device=DEV).to(dtype)
     mdg.zero_pad_rows(out, torch.tensor([0, 10, 20, 30, 500], dtype=torch.int32, device=DEV), E)
     assert torch.all(out[:500] == 1) and torch.all(out[500:] == 0)
@@ -195,8 +195,9 @@ def test_inference_tensors():
 def test_malformed_offsets_act_as_clamped(bad):
     """The kernels clamp each offset to [0, m_rows] and take the running maximum, so a
     malformed array reads and writes nothing out of bounds and gives, bit for bit, the
-    result of its sanitised form (every host-side size depends on m_rows and the group
-    count only, which any sanitised array respects)."""
+    result of its sanitised form, the zero fill of the padding rows included.  Every
+    host-side size depends on m_rows and the group count only, which any sanitised
+    array respects."""
     M, N, K = 3000, 520, 328
     d = make_inputs(sizes=[600] * 5, N=N, K=K, seed=21, device=DEV, tensors=("x", "w", "g", "main_grad"))
     clean = np.maximum.accumulate(np.clip(np.asarray(bad, dtype=np.int64), 0, M))
@@ -209,8 +210,11 @@ def test_malformed_offsets_act_as_clamped(bad):
         dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], offs, out_dtype=torch.float32)
         mg = d["main_grad"].clone()
         mdg.grouped_det_gemm_wgrad(d["g"], d["x"], offs, out=mg, accumulate=True)
+        z = torch.full((M, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+        mdg.zero_pad_rows(z, offs, 5)
         torch.cuda.synchronize()
-        return [y.view(torch.int16), dx.view(torch.int16), dw.view(torch.int32), mg.view(torch.int32)]
+        return [y.view(torch.int16), dx.view(torch.int16), dw.view(torch.int32), mg.view(torch.int32),
+                z.view(torch.int16)]
 
     got = run(torch.tensor(bad, dtype=torch.int32, device=DEV))
     want = run(torch.tensor(clean, dtype=torch.int32, device=DEV))
@@ -220,5 +224,8 @@ def test_malformed_offsets_act_as_clamped(bad):
     sizes = np.diff(np.concatenate([[0], clean]))
     for e in np.flatnonzero(sizes == 0):
         assert torch.all(got[2][e] == 0)
+    seven = torch.tensor(7.0, dtype=torch.bfloat16).view(torch.int16).item()
     if clean[-1] < M:
-        assert torch.all(got[0][clean[-1]:] == torch.tensor(7.0, dtype=torch.bfloat16).view(torch.int16).item())
+        assert torch.all(got[0][clean[-1]:] == seven)
+    # the zero fill covers exactly the rows past the sanitised last end
+    assert torch.all(got[4][:clean[-1]] == seven) and torch.all(got[4][clean[-1]:] == 0)
