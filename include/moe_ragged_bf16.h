@@ -64,7 +64,15 @@
 extern "C" {
 #endif
 
-#define MDG_ABI_VERSION 5
+/* Entry points are the library's only exported symbols (it is built with
+   hidden visibility by default). */
+#if defined(__GNUC__) || defined(__clang__)
+#define MDG_API __attribute__((visibility("default")))
+#else
+#define MDG_API
+#endif
+
+#define MDG_ABI_VERSION 6
 
 typedef enum {
   MDG_OK = 0,
@@ -79,10 +87,11 @@ typedef enum {
 typedef enum { MDG_BF16 = 0, MDG_FP32 = 1 } mdg_dtype;
 
 /* Version of this ABI (MDG_ABI_VERSION of the header the library was built with). */
-int mdg_abi_version(void);
+MDG_API int grouped_det_gemm_abi_version(void);
 
-/* Static, NUL-terminated description of a status code (never NULL). */
-const char* mdg_status_string(int status);
+/* Static, NUL-terminated description of a status code (never NULL; an unknown
+   code gives "unknown status"). */
+MDG_API const char* grouped_det_gemm_status_string(int status);
 
 /*
  * Bytes of device workspace grouped_det_gemm_fwd (resp. _dgrad) needs for these
@@ -90,10 +99,10 @@ const char* mdg_status_string(int status);
  * below (at most 8 KiB + 64 MiB).  It depends on the sizes only (never on offs or
  * the device).  Returns 0 for invalid sizes.
  */
-size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
-                                            int32_t num_groups);
-size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
-                                              int32_t num_groups);
+MDG_API size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                                    int32_t num_groups);
+MDG_API size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                                      int32_t num_groups);
 
 /*
  * fwd: Y[s_e:t_e] = X[s_e:t_e] @ W[e]^T  (API page, operations table, "fwd").
@@ -112,9 +121,9 @@ size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t
  * still a fixed function of the inputs: bitwise identical from run to run.
  * m_rows == 0 enqueues nothing.  y must not overlap x, w, offs or the workspace.
  */
-int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y,
-                         int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                         void* workspace, size_t workspace_bytes, void* stream);
+MDG_API mdg_status grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y,
+                                        int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dgrad: dX[s_e:t_e] = G[s_e:t_e] @ W[e], W read in place (API page, operations
@@ -125,9 +134,9 @@ int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void
  *      bytes; the same tail split applies (the reduction here runs over n).
  * m_rows == 0 enqueues nothing.  dx must not overlap g, w, offs or the workspace.
  */
-int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
-                           int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                           void* workspace, size_t workspace_bytes, void* stream);
+MDG_API mdg_status grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
+                                          int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace grouped_det_gemm_wgrad needs for these sizes: a small
@@ -135,8 +144,8 @@ int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, vo
  * on the sizes only (never on offs or the device), so the host can allocate it
  * without a sync.  Returns 0 for invalid sizes.
  */
-size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
-                                              int32_t num_groups);
+MDG_API size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k,
+                                                      int32_t num_groups);
 
 /*
  * wgrad: dW[e] = G[s_e:t_e]^T @ X[s_e:t_e]  (API page, operations table, "wgrad";
@@ -159,18 +168,18 @@ size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t
  * chunk order by a second kernel on the same stream.  dw must not overlap g, x,
  * offs or the workspace.
  */
-int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
-                           int dw_dtype, int accumulate,
-                           int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                           void* workspace, size_t workspace_bytes, void* stream);
+MDG_API mdg_status grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
+                                          int dw_dtype, int accumulate,
+                                          int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Rows per chunk of the wgrad row split for these sizes (a pure function of the
  * sizes; exposed so tests can build cases with and without a split).
  * Returns 0 for invalid sizes.
  */
-int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
-                                          int32_t num_groups);
+MDG_API int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
+                                                  int32_t num_groups);
 
 /*
  * Zero fill of the rows that belong to no group: out[r, :] = 0 for
@@ -187,8 +196,8 @@ int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k,
  *     m_indptr + 1.
  * m_rows == 0 enqueues nothing.  out must not overlap offs.
  */
-int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
-                                   int32_t num_groups, void* stream);
+MDG_API mdg_status grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
+                                                  int32_t num_groups, void* stream);
 
 /*
  * Prepared launches (Cake ragged BF16 grouped GEMM API page, "Prepared
@@ -229,21 +238,21 @@ typedef struct {
   int64_t workspace_bytes;  /* workspace bytes the launch uses */
 } mdg_launch_info;
 
-int grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y,
-                                 int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                                 void* workspace, size_t workspace_bytes, mdg_launch** launch);
-int grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
-                                   int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                                   void* workspace, size_t workspace_bytes, mdg_launch** launch);
-int grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
-                                   int dw_dtype, int accumulate,
-                                   int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
-                                   void* workspace, size_t workspace_bytes, mdg_launch** launch);
-int grouped_det_gemm_launch(const mdg_launch* launch, void* stream);
+MDG_API mdg_status grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y,
+                                                int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                                void* workspace, size_t workspace_bytes, mdg_launch** launch);
+MDG_API mdg_status grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx,
+                                                  int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                                  void* workspace, size_t workspace_bytes, mdg_launch** launch);
+MDG_API mdg_status grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw,
+                                                  int dw_dtype, int accumulate,
+                                                  int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                                  void* workspace, size_t workspace_bytes, mdg_launch** launch);
+MDG_API mdg_status grouped_det_gemm_launch(const mdg_launch* launch, void* stream);
 /* Describes a prepared launch (MDG_EINVAL for NULL arguments). */
-int grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info);
+MDG_API mdg_status grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info);
 /* Releases a prepared launch (NULL is ignored).  Work already enqueued is unaffected. */
-void grouped_det_gemm_launch_free(mdg_launch* launch);
+MDG_API void grouped_det_gemm_launch_free(mdg_launch* launch);
 
 #ifdef __cplusplus
 }

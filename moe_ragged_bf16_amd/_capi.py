@@ -16,8 +16,8 @@ MDG_OK, MDG_EINVAL, MDG_EUNSUPPORTED, MDG_EOVERLAP, MDG_EWORKSPACE, MDG_EHIP, MD
 MDG_BF16, MDG_FP32 = 0, 1
 
 EXPORTED = (
-    "mdg_abi_version",
-    "mdg_status_string",
+    "grouped_det_gemm_abi_version",
+    "grouped_det_gemm_status_string",
     "grouped_det_gemm_fwd",
     "grouped_det_gemm_dgrad",
     "grouped_det_gemm_fwd_workspace_bytes",
@@ -69,10 +69,10 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                 "(python -m moe_ragged_bf16_amd.build)")
         lib = ctypes.CDLL(path)
         i32, i64, vp, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
-        lib.mdg_abi_version.restype = ctypes.c_int
-        lib.mdg_abi_version.argtypes = []
-        lib.mdg_status_string.restype = ctypes.c_char_p
-        lib.mdg_status_string.argtypes = [ctypes.c_int]
+        lib.grouped_det_gemm_abi_version.restype = ctypes.c_int
+        lib.grouped_det_gemm_abi_version.argtypes = []
+        lib.grouped_det_gemm_status_string.restype = ctypes.c_char_p
+        lib.grouped_det_gemm_status_string.argtypes = [ctypes.c_int]
         for name in ("grouped_det_gemm_fwd", "grouped_det_gemm_dgrad"):
             f = getattr(lib, name)
             f.restype = ctypes.c_int
@@ -109,7 +109,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
 
 
 def status_string(status: int) -> str:
-    return load_library().mdg_status_string(status).decode()
+    return load_library().grouped_det_gemm_status_string(status).decode()
 
 
 def check(entry: str, status: int) -> None:

@@ -6,7 +6,9 @@ links them into the package directory.  Run ``python -m moe_ragged_bf16_amd.buil
 from __future__ import annotations
 
 import os
+import re
 import shutil
+import tempfile
 import subprocess
 import sys
 
@@ -26,9 +28,17 @@ HIP_FLAGS = [
     "-shared",
     # the accumulate epilogue and the split reduction are plain IEEE adds
     "-ffp-contract=off",
-    # never emit packed fp32 arithmetic
+    # never emit packed fp32 arithmetic (v_pk_add/mul/fma_f32).  The feature
+    # belongs to the gfx950 device pass; the host pass prints that it does not
+    # know it and ignores it.  check_no_packed_fp32() verifies the result.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # export only the entry points the public header marks MDG_API
+    "-fvisibility=hidden",
 ]
+
+LLVM_BIN = "/opt/rocm/llvm/bin"
+DEVICE_TARGET = "hipv4-amdgcn-amd-amdhsa--gfx950"
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma)_f32\b")
 
 
 def hipcc() -> str:
@@ -51,8 +61,41 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError("hipcc failed building %s" % LIB_NAME)
+    try:
+        check_no_packed_fp32(tmp)
+    except Exception:
+        os.unlink(tmp)
+        raise
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
+
+
+def device_assembly(lib_path: str = LIB_PATH) -> str:
+    """AMD assembly of the gfx950 code object built into `lib_path` (its
+    .hip_fatbin section, unbundled and disassembled with ROCm's LLVM tools)."""
+    with tempfile.TemporaryDirectory() as d:
+        fat = os.path.join(d, "fatbin.bin")
+        co = os.path.join(d, "gfx950.co")
+        for cmd in ([os.path.join(LLVM_BIN, "llvm-objcopy"), "--dump-section", ".hip_fatbin=" + fat, lib_path],
+                    [os.path.join(LLVM_BIN, "clang-offload-bundler"), "--unbundle", "--type=o", "--input=" + fat,
+                     "--targets=" + DEVICE_TARGET, "--output=" + co]):
+            res = subprocess.run(cmd, capture_output=True, text=True)
+            if res.returncode != 0:
+                raise RuntimeError("extracting the gfx950 code object failed: " + res.stderr)
+        res = subprocess.run([os.path.join(LLVM_BIN, "llvm-objdump"), "-d", co], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("llvm-objdump failed: " + res.stderr)
+        return res.stdout
+
+
+def check_no_packed_fp32(lib_path: str = LIB_PATH) -> int:
+    """Raises if the built device code holds a packed fp32 add, multiply or
+    fma; returns the number of MFMA instructions seen (a sanity count)."""
+    asm = device_assembly(lib_path)
+    bad = [ln.strip() for ln in asm.splitlines() if PACKED_FP32.search(ln)]
+    if bad:
+        raise RuntimeError("packed fp32 arithmetic in the gfx950 code: %d instructions, e.g. %s" % (len(bad), bad[0]))
+    return sum(1 for ln in asm.splitlines() if "v_mfma" in ln)
 
 
 C_SMOKE_SRC = os.path.join(ROOT, "tests", "c_abi_smoke.cpp")

@@ -170,14 +170,22 @@ struct mdg_launch {
 namespace mdg {
 namespace {
 
-int prepare_fwd_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
-                      int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
-                      mdg_launch* l) {
+// The checks of fwd/dgrad that need neither the workspace nor the device.
+int check_fwd_dgrad(const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows, int64_t n,
+                    int64_t k, int32_t num_groups) {
   int st = check_sizes(m_rows, n, k, num_groups);
   if (st != MDG_OK) return st;
   // Row-indexed tensors may be NULL when there are no rows (never dereferenced).
   if (!w || !offs || (m_rows > 0 && (!a || !out))) return MDG_EINVAL;
   if (!aligned16(a) || !aligned16(w) || !aligned4(offs) || !aligned16(out)) return MDG_EINVAL;
+  return MDG_OK;
+}
+
+int prepare_fwd_dgrad(Op op, const void* a, const void* w, const int32_t* offs, void* out, int64_t m_rows,
+                      int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
+                      mdg_launch* l) {
+  int st = check_fwd_dgrad(a, w, offs, out, m_rows, n, k, num_groups);
+  if (st != MDG_OK) return st;
   const size_t need = fwd_dgrad_workspace(op, m_rows, n, k, num_groups);
   if (!workspace || workspace_bytes < need) return MDG_EWORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MDG_EINVAL;
@@ -307,6 +315,16 @@ int enqueue(const mdg_launch& l, hipStream_t s) {
   return MDG_OK;
 }
 
+int publish(int st, const mdg_launch& l, mdg_launch** out) {
+  if (st != MDG_OK) return st;
+  mdg_launch* h = new (std::nothrow) mdg_launch(l);
+  if (!h) return MDG_ENOMEM;
+  *out = h;
+  return MDG_OK;
+}
+
+mdg_status status(int st) { return static_cast<mdg_status>(st); }
+
 int kernels_of(const mdg_launch& l) {
   if (l.gemm_grid == 0) return 0;
   return 1 + (l.tail_gy > 0) + (l.red_gy > 0);
@@ -319,9 +337,9 @@ using namespace mdg;
 
 extern "C" {
 
-int mdg_abi_version(void) { return MDG_ABI_VERSION; }
+MDG_API int grouped_det_gemm_abi_version(void) { return MDG_ABI_VERSION; }
 
-const char* mdg_status_string(int s) {
+MDG_API const char* grouped_det_gemm_status_string(int s) {
   switch (s) {
     case MDG_OK: return "ok";
     case MDG_EINVAL: return "invalid argument (null or misaligned pointer, negative size or bad enum)";
@@ -334,104 +352,94 @@ const char* mdg_status_string(int s) {
   }
 }
 
-size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+MDG_API size_t grouped_det_gemm_fwd_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
   return fwd_dgrad_workspace(kFwd, m_rows, n, k, num_groups);
 }
 
-size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+MDG_API size_t grouped_det_gemm_dgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
   return fwd_dgrad_workspace(kDgrad, m_rows, n, k, num_groups);
 }
 
-int grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
+MDG_API mdg_status grouped_det_gemm_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
                          int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
                          void* stream) {
   mdg_launch l;
   const int st = prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, &l);
-  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+  return status(st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream)));
 }
 
-int grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
+MDG_API mdg_status grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
                            int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
                            void* stream) {
   mdg_launch l;
   const int st = prepare_fwd_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes, &l);
-  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+  return status(st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream)));
 }
 
-int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+MDG_API int64_t grouped_det_gemm_wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
   return wgrad_chunk_rows(m_rows, n, k, num_groups);
 }
 
-size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
+MDG_API size_t grouped_det_gemm_wgrad_workspace_bytes(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups) {
   if (check_sizes(m_rows, n, k, num_groups) != MDG_OK) return 0;
   return wgrad_workspace(m_rows, n, k, num_groups).total;
 }
 
-int grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
+MDG_API mdg_status grouped_det_gemm_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
                            int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
                            void* workspace, size_t workspace_bytes, void* stream) {
   mdg_launch l;
   const int st = prepare_wgrad(g, x, offs, dw, dw_dtype, accumulate, m_rows, n, k, num_groups, workspace,
                                workspace_bytes, &l);
-  return st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream));
+  return status(st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream)));
 }
 
-namespace {
-int publish(int st, const mdg_launch& l, mdg_launch** out) {
-  if (st != MDG_OK) return st;
-  mdg_launch* h = new (std::nothrow) mdg_launch(l);
-  if (!h) return MDG_ENOMEM;
-  *out = h;
-  return MDG_OK;
-}
-}  // namespace
-
-int grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
+MDG_API mdg_status grouped_det_gemm_prepare_fwd(const void* x, const void* w, const int32_t* offs, void* y, int64_t m_rows,
                                  int64_t n, int64_t k, int32_t num_groups, void* workspace,
                                  size_t workspace_bytes, mdg_launch** launch) {
-  if (!launch) return MDG_EINVAL;
+  if (!launch) return status(MDG_EINVAL);
   *launch = nullptr;
   mdg_launch l;
-  return publish(prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, &l),
-                 l, launch);
+  return status(publish(prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, workspace, workspace_bytes, &l),
+                 l, launch));
 }
 
-int grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
+MDG_API mdg_status grouped_det_gemm_prepare_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
                                    int64_t n, int64_t k, int32_t num_groups, void* workspace,
                                    size_t workspace_bytes, mdg_launch** launch) {
-  if (!launch) return MDG_EINVAL;
+  if (!launch) return status(MDG_EINVAL);
   *launch = nullptr;
   mdg_launch l;
-  return publish(prepare_fwd_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes,
+  return status(publish(prepare_fwd_dgrad(kDgrad, g, w, offs, dx, m_rows, n, k, num_groups, workspace, workspace_bytes,
                                    &l),
-                 l, launch);
+                 l, launch));
 }
 
-int grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
+MDG_API mdg_status grouped_det_gemm_prepare_wgrad(const void* g, const void* x, const int32_t* offs, void* dw, int dw_dtype,
                                    int accumulate, int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
                                    void* workspace, size_t workspace_bytes, mdg_launch** launch) {
-  if (!launch) return MDG_EINVAL;
+  if (!launch) return status(MDG_EINVAL);
   *launch = nullptr;
   mdg_launch l;
-  return publish(prepare_wgrad(g, x, offs, dw, dw_dtype, accumulate, m_rows, n, k, num_groups, workspace,
+  return status(publish(prepare_wgrad(g, x, offs, dw, dw_dtype, accumulate, m_rows, n, k, num_groups, workspace,
                                workspace_bytes, &l),
-                 l, launch);
+                 l, launch));
 }
 
-int grouped_det_gemm_launch(const mdg_launch* launch, void* stream) {
-  if (!launch) return MDG_EINVAL;
-  if (launch->gemm_grid == 0) return MDG_OK;  // nothing to enqueue
+MDG_API mdg_status grouped_det_gemm_launch(const mdg_launch* launch, void* stream) {
+  if (!launch) return status(MDG_EINVAL);
+  if (launch->gemm_grid == 0) return status(MDG_OK);  // nothing to enqueue
   int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess) return MDG_EHIP;
-  if (dev != launch->device) return MDG_EINVAL;
-  return enqueue(*launch, static_cast<hipStream_t>(stream));
+  if (hipGetDevice(&dev) != hipSuccess) return status(MDG_EHIP);
+  if (dev != launch->device) return status(MDG_EINVAL);
+  return status(enqueue(*launch, static_cast<hipStream_t>(stream)));
 }
 
-int grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info) {
-  if (!launch || !info) return MDG_EINVAL;
+MDG_API mdg_status grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info) {
+  if (!launch || !info) return status(MDG_EINVAL);
   mdg_launch_info r;
   memset(&r, 0, sizeof(r));
   r.op = launch->op;
@@ -444,33 +452,33 @@ int grouped_det_gemm_launch_info(const mdg_launch* launch, mdg_launch_info* info
   r.tail_slots = launch->op == kWgrad ? 0 : launch->p.tail_slots;
   r.workspace_bytes = launch->workspace_bytes;
   *info = r;
-  return MDG_OK;
+  return status(MDG_OK);
 }
 
-void grouped_det_gemm_launch_free(mdg_launch* launch) { delete launch; }
+MDG_API void grouped_det_gemm_launch_free(mdg_launch* launch) { delete launch; }
 
-int grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
+MDG_API mdg_status grouped_det_gemm_zero_pad_rows(void* out, const int32_t* offs, int64_t m_rows, int64_t row_bytes,
                                    int32_t num_groups, void* stream) {
-  if (m_rows < 0 || row_bytes <= 0 || num_groups <= 0) return MDG_EINVAL;
-  if (num_groups > kMaxGroups) return MDG_EUNSUPPORTED;
-  if (row_bytes % 16 != 0 || m_rows > kMaxRows || row_bytes > (int64_t)1 << 24) return MDG_EUNSUPPORTED;
-  if (!offs || (m_rows > 0 && !out)) return MDG_EINVAL;
-  if (!aligned16(out) || !aligned4(offs)) return MDG_EINVAL;
-  if (overlaps(range_of(out, m_rows * row_bytes), range_of(offs, (int64_t)num_groups * 4))) return MDG_EOVERLAP;
-  if (m_rows == 0) return MDG_OK;
+  if (m_rows < 0 || row_bytes <= 0 || num_groups <= 0) return status(MDG_EINVAL);
+  if (num_groups > kMaxGroups) return status(MDG_EUNSUPPORTED);
+  if (row_bytes % 16 != 0 || m_rows > kMaxRows || row_bytes > (int64_t)1 << 24) return status(MDG_EUNSUPPORTED);
+  if (!offs || (m_rows > 0 && !out)) return status(MDG_EINVAL);
+  if (!aligned16(out) || !aligned4(offs)) return status(MDG_EINVAL);
+  if (overlaps(range_of(out, m_rows * row_bytes), range_of(offs, (int64_t)num_groups * 4))) return status(MDG_EOVERLAP);
+  if (m_rows == 0) return status(MDG_OK);
 
   DeviceInfo dev;
   int device = -1;
   const int st = query_device(&dev, &device);
-  if (st != MDG_OK) return st;
-  if (!dev.gfx950) return MDG_EUNSUPPORTED;
+  if (st != MDG_OK) return status(st);
+  if (!dev.gfx950) return status(MDG_EUNSUPPORTED);
   const int64_t vecs = m_rows * (row_bytes / 16);
   const int64_t cap = 2 * (int64_t)(dev.cus > 0 ? dev.cus : 256);
   const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(cap, (vecs + kThreads - 1) / kThreads));
   if (launch_zero_rows(out, offs, num_groups, m_rows, row_bytes, grid, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
-    return MDG_EHIP;
-  return MDG_OK;
+    return status(MDG_EHIP);
+  return status(MDG_OK);
 }
 
 }  // extern "C"

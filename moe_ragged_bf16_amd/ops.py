@@ -81,10 +81,13 @@ def _workspace(workspace: Optional[torch.Tensor], need: int, device) -> torch.Te
     """The caller's workspace (checked) or a fresh one from torch's allocator."""
     if workspace is None:
         return torch.empty(max(need, 256), dtype=torch.uint8, device=device)
-    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8 or \
+            not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous uint8 tensor")
     if workspace.numel() < need:
         raise ValueError(f"workspace too small: {workspace.numel()} < {need} bytes")
+    if workspace.device.type != "cuda":
+        raise ValueError(f"workspace must be on a ROCm device, got {workspace.device}")
     return workspace
 
 
@@ -202,14 +205,13 @@ def grouped_det_gemm_wgrad(g: torch.Tensor, x: torch.Tensor, offs: torch.Tensor,
         raise ValueError(f"out must have shape {(E, N, K)}")
     _same_device(g, x, offs, out)
     op = _offs_ptr(offs, E)
-    need = wgrad_workspace_bytes(M, N, K, E)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=g.device)
+    ws = _workspace(workspace, wgrad_workspace_bytes(M, N, K, E), g.device)
+    _same_device(g, ws)
     dt_code = _capi.MDG_FP32 if out.dtype == torch.float32 else _capi.MDG_BF16
     with torch.cuda.device(g.device):
         st = _capi.load_library().grouped_det_gemm_wgrad(
             g.data_ptr(), x.data_ptr(), op, out.data_ptr(), dt_code, int(accumulate),
-            M, N, K, E, workspace.data_ptr(), workspace.numel(), _stream_handle(g))
+            M, N, K, E, ws.data_ptr(), ws.numel(), _stream_handle(g))
     _capi.check("grouped_det_gemm_wgrad", st)
     if given:
         _written(out)

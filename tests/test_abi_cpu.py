@@ -23,7 +23,8 @@ OK, EINVAL, EUNSUP, EOVERLAP, EWS, EHIP, ENOMEM = range(7)
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"defined"})
+    src = "\n".join(ln for ln in src.splitlines() if not ln.lstrip().startswith("#"))
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -38,8 +39,26 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, n), n
 
 
+def test_library_exports_exactly_the_declared_symbols(lib):
+    """Built with hidden visibility: the dynamic symbol table holds the header's
+    entry points and nothing else of the library's own code."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _capi._build.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.split() and ln.split()[1] in "TtWw"}
+    ours = {n for n in exported if not n.startswith("_")}   # compiler/runtime glue starts with _
+    assert ours == set(declared_functions()), sorted(ours ^ set(declared_functions()))
+
+
+def test_device_code_has_no_packed_fp32_arithmetic():
+    """The library's gfx950 code object, disassembled, holds MFMAs and no packed
+    fp32 add, multiply or fma (the build flag that forbids them is effective)."""
+    from moe_ragged_bf16_amd import build
+    assert build.check_no_packed_fp32(build.LIB_PATH) > 1000
+
+
 def test_abi_version_and_status_strings(lib):
-    assert lib.mdg_abi_version() == 5
+    assert lib.grouped_det_gemm_abi_version() == 6
     for s in range(7):
         assert mdg.status_string(s)
     assert mdg.status_string(99) == "unknown status"

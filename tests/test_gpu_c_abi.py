@@ -1,5 +1,6 @@
 """The C ABI from a C++ caller with no Python in between (tests/c_abi_smoke.cpp:
-workspace query, refusals, a prepared fwd launched twice, a closed-form check)."""
+workspace queries, refusals, a prepared fwd launched twice, one-shot dgrad,
+wgrad and both fused accumulates, each against a closed form)."""
 import os
 import subprocess
 
