@@ -126,6 +126,29 @@ MDG_API mdg_status grouped_det_gemm_fwd(const void* x, const void* w, const int3
                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fwd for callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * arguments and results of grouped_det_gemm_fwd, bit for bit, without a
+ * workspace argument.  Its scratch (the tail plan and the fp32 partial tiles
+ * of the tail split) is a static device array of the library, 64 MiB + 8 KiB,
+ * the largest workspace any fwd call needs, so every size grouped_det_gemm_fwd
+ * accepts is accepted (a size needing more would get MDG_EWORKSPACE).  Each
+ * device the library runs on holds its own copy from the library's loading on
+ * that device until the process ends; its address is looked up once per
+ * device, at the first call.  No call allocates or frees memory, synchronises
+ * or copies; only kernels are enqueued on `stream`.
+ * Every call on one device shares that device's array, and nothing in it needs
+ * to start cleared: each call writes the plan and partial tiles before reading
+ * them, in stream order.  Calls that may overlap on one device (on different
+ * streams, or from different threads without ordering) RACE on the array and
+ * give undefined results: order them on one stream.
+ * m_rows == 0 enqueues nothing.  y must not overlap x, w or offs.
+ */
+MDG_API mdg_status grouped_det_gemm_fwd_noalloc(const void* x, const void* w, const int32_t* offs, void* y,
+                                                int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                                void* stream);
+
+/*
  * dgrad: dX[s_e:t_e] = G[s_e:t_e] @ W[e], W read in place (API page, operations
  * table, "dgrad").
  *   g  [m_rows, n] bf16, read.        w [num_groups, n, k] bf16, read.

@@ -20,6 +20,7 @@ EXPORTED = (
     "grouped_det_gemm_status_string",
     "grouped_det_gemm_fwd",
     "grouped_det_gemm_dgrad",
+    "grouped_det_gemm_fwd_noalloc",
     "grouped_det_gemm_fwd_workspace_bytes",
     "grouped_det_gemm_dgrad_workspace_bytes",
     "grouped_det_gemm_wgrad",
@@ -77,6 +78,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
             f = getattr(lib, name)
             f.restype = ctypes.c_int
             f.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, sz, vp]
+        lib.grouped_det_gemm_fwd_noalloc.restype = ctypes.c_int
+        lib.grouped_det_gemm_fwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp]
         for name in ("grouped_det_gemm_fwd_workspace_bytes", "grouped_det_gemm_dgrad_workspace_bytes"):
             f = getattr(lib, name)
             f.restype = sz

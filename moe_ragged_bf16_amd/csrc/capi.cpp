@@ -370,6 +370,26 @@ MDG_API mdg_status grouped_det_gemm_fwd(const void* x, const void* w, const int3
   return status(st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream)));
 }
 
+MDG_API mdg_status grouped_det_gemm_fwd_noalloc(const void* x, const void* w, const int32_t* offs, void* y,
+                                                int64_t m_rows, int64_t n, int64_t k, int32_t num_groups,
+                                                void* stream) {
+  int st = check_fwd_dgrad(x, w, offs, y, m_rows, n, k, num_groups);
+  if (st != MDG_OK) return status(st);
+  if (m_rows == 0) return status(MDG_OK);  // nothing to enqueue (as grouped_det_gemm_fwd)
+  // the static array holds the largest fwd workspace, so no valid size is refused here
+  if (fwd_dgrad_workspace(kFwd, m_rows, n, k, num_groups) > kFwdScratchBytes) return status(MDG_EWORKSPACE);
+  DeviceInfo dev;
+  int device = -1;
+  st = query_device(&dev, &device);
+  if (st != MDG_OK) return status(st);
+  if (!dev.gfx950) return status(MDG_EUNSUPPORTED);
+  void* ws = nullptr;
+  if (fwd_scratch_address(device, &ws) != hipSuccess) return status(MDG_EHIP);
+  mdg_launch l;
+  st = prepare_fwd_dgrad(kFwd, x, w, offs, y, m_rows, n, k, num_groups, ws, kFwdScratchBytes, &l);
+  return status(st != MDG_OK ? st : enqueue(l, static_cast<hipStream_t>(stream)));
+}
+
 MDG_API mdg_status grouped_det_gemm_dgrad(const void* g, const void* w, const int32_t* offs, void* dx, int64_t m_rows,
                            int64_t n, int64_t k, int32_t num_groups, void* workspace, size_t workspace_bytes,
                            void* stream) {

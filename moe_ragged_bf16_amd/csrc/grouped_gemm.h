@@ -25,6 +25,10 @@ constexpr int64_t kMaxRows = 4000000;  // m_rows limit (row indices and group si
 constexpr int kBalanceSlots = 256;
 constexpr int kMaxSplit = 8;
 constexpr int kTailHeadBytes = 8192;  // plan + per-tail-unit descriptors, at the workspace head
+// The largest workspace a fwd or dgrad call needs: the head and kBalanceSlots
+// fp32 partial tiles.  The allocation-free fwd entry keeps this in a static
+// device array.
+constexpr size_t kFwdScratchBytes = (size_t)kTailHeadBytes + (size_t)kBalanceSlots * kTileI * kTileJ * sizeof(float);
 
 enum Op : int { kFwd = 0, kDgrad = 1, kWgrad = 2 };
 
@@ -57,6 +61,11 @@ hipError_t launch_wgrad_reduce(const GemmParams& p, int grid_x, int grid_y, hipS
 hipError_t launch_tail_reduce(const GemmParams& p, int grid_x, int grid_y, hipStream_t stream);
 hipError_t launch_zero_rows(void* out, const int32_t* offs, int num_groups, int64_t m_rows, int64_t row_bytes,
                             int grid, hipStream_t stream);
+
+// Address of this device's copy of the static scratch array of the
+// allocation-free fwd entry (kFwdScratchBytes, 256-byte aligned), looked up
+// once per device with that device current (grouped_gemm_kernels.hip).
+hipError_t fwd_scratch_address(int device, void** ptr);
 
 // Host-side sizing helpers (capi.cpp).
 int64_t wgrad_chunk_rows(int64_t m_rows, int64_t n, int64_t k, int32_t num_groups);

@@ -47,7 +47,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "grouped_gemm.h"
+
+// Scratch of the allocation-free fwd entry point (grouped_det_gemm_fwd_noalloc):
+// the tail plan head and the fp32 partial tiles of the tail split, sized for
+// the largest fwd call.  Each device holds its own copy for the life of the
+// process.  Host code must not pass this name to a kernel (on the host it is a
+// stand-in, not a device address): it uses the per-device address that
+// fwd_scratch_address() looks up below.  Nothing in it has to start at zero:
+// the GEMM kernel writes the plan and the partial tiles before the reduce
+// kernel, next on the same stream, reads them.
+static __device__ __align__(256) uint8_t scratch[mdg::kFwdScratchBytes];
 
 namespace mdg {
 namespace {
@@ -1566,6 +1578,27 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(uint8_t* out, const
 }
 
 }  // namespace
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t fwd_scratch_address(int device, void** ptr) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[device], [device]() {
+    void* p = nullptr;
+    g_scratch_err[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[device] = p;
+  });
+  if (g_scratch_err[device] != hipSuccess) return g_scratch_err[device];
+  if (g_scratch_ptr[device] == nullptr || (reinterpret_cast<uintptr_t>(g_scratch_ptr[device]) & 255u) != 0)
+    return hipErrorInvalidSymbol;
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 hipError_t launch_gemm(Op op, const GemmParams& p, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(kThreads);

@@ -290,3 +290,20 @@ def test_missing_library_fails_loudly(monkeypatch):
         mdg.wgrad_workspace_bytes(512, 256, 256, 4)
     with pytest.raises(ImportError):
         mdg.load_library()
+
+
+def test_fwd_noalloc_refusals_before_the_device(lib):
+    """The allocation-free fwd takes fwd's arguments without a workspace and
+    refuses the same bad ones before touching the device; no rows: nothing to do."""
+    f = lib.grouped_det_gemm_fwd_noalloc
+
+    def call(a=A, w=B, o=C, d=D, M=8, N=256, K=256, E=4):
+        return f(a, w, o, d, M, N, K, E, None)
+
+    assert call(M=-1) == EINVAL
+    assert call(N=100) == EUNSUP
+    assert call(E=1025) == EUNSUP
+    assert call(w=0) == EINVAL
+    assert call(a=A + 8) == EINVAL
+    assert call(o=C + 2) == EINVAL
+    assert call(M=0, a=0, d=0) == OK
