@@ -225,7 +225,6 @@ int prepare_fwd_dgrad(Op op, const void* a, const void* w, const int32_t* offs, 
   p.tail_head = reinterpret_cast<int32_t*>(ws);
   p.partial = reinterpret_cast<float*>(ws + kTailHeadBytes);
   p.tail_slots = (int32_t)slots;
-  p.skinny_rows = kSkinnyMaxRows;
   l->gemm_grid = persistent_grid(units_ub + slots, dev.cus);
   // Split tail units (at most kBalanceSlots / 2 of them, as each has >= 2
   // pieces): the reduce kernel reads the plan the GEMM kernel wrote and exits

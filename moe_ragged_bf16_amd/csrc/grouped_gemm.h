@@ -17,10 +17,6 @@ constexpr int kKAlign = 8;       // k must be a multiple of this: rows of whole 
 constexpr int kNAlign = 8;       // n likewise (partial tiles and partial reduction stages are masked)
 constexpr int kChunkAlign = 64;  // wgrad chunk rows are a multiple of this
 constexpr int kPairRows = 2048;  // fwd loads stages in pairs when m_rows >= kPairRows * num_groups
-// fwd/dgrad: a group of at most skinny_rows rows is cut into row tiles of
-// kSkinnyTileRows instead of kTileI (see the skinny units in the kernels).
-constexpr int kSkinnyTileRows = 32;
-constexpr int kSkinnyMaxRows = 64;  // the skinny_rows the C ABI passes
 constexpr int kThreads = 256;    // 4 waves of 64
 constexpr int kMaxGroups = 1024; // groups held in each workgroup's LDS table
 constexpr int64_t kMaxRows = 4000000;  // m_rows limit (row indices and group sizes stay well inside int32)
@@ -48,7 +44,6 @@ struct GemmParams {
   int32_t out_fp32;       // wgrad: dW is fp32
   int32_t accumulate;     // wgrad: fp32 dW = RN32(dW + product); bf16 dW = RNE(RN32(dW + RNE(product)))
   int32_t tail_slots;     // fwd/dgrad: partial tiles the workspace holds (0: no tail split)
-  int32_t skinny_rows;    // fwd/dgrad: groups of at most this many rows use skinny units (0: none)
   int32_t* tail_head;     // fwd/dgrad: kTailHeadBytes of workspace: the tail plan for the reduce kernel
 };
 

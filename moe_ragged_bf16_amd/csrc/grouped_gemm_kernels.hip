@@ -153,19 +153,12 @@ __device__ __forceinline__ UnitShape unit_shape(const GemmParams& p) {
   return s;
 }
 
-// Rows of a fwd/dgrad row tile of a group of m rows: skinny tiles for groups
-// of at most skinny_rows rows, whole tiles otherwise.
-__device__ __forceinline__ int row_tile_rows(int m, const GemmParams& p) {
-  return m <= p.skinny_rows ? kSkinnyTileRows : kTileI;
-}
-
 // Slices of a group: fwd/dgrad row tiles; wgrad row chunks (an empty expert
 // still has one slice: its zero dW tiles).
 template <int OP>
 __device__ __forceinline__ int group_slices(int m, const GemmParams& p) {
   if (OP == kWgrad) return m == 0 ? 1 : (m + p.chunk_rows - 1) / p.chunk_rows;
-  const int th = row_tile_rows(m, p);
-  return (m + th - 1) / th;
+  return (m + kTileI - 1) / kTileI;
 }
 
 // LDS table of the groups.  Thread t handles groups 4t .. 4t+3.
@@ -778,7 +771,6 @@ __device__ __forceinline__ void epilogue_accumulate_bf16(const Acc& acc, const O
 // ---------------------------------------------------------------------------
 struct Unit {
   int valid;
-  int skinny;    // fwd/dgrad: a skinny unit (kSkinnyTileRows rows; see Skinny)
   int nk;        // reduction stages of 32, rounded up to a multiple of 4 (extra stages load zeros)
   int nkr;       // stages that hold data (nk - 3 <= nkr <= nk); the steps of the others are skipped
   Operand a, b;
@@ -802,14 +794,11 @@ __device__ __forceinline__ Unit decode_unit(const GemmParams& p, const GroupTabl
   const uint8_t* A = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* B = reinterpret_cast<const uint8_t*>(p.b);
   x.mode = kStoreBf16;
-  x.skinny = 0;
   if (OP == kFwd || OP == kDgrad) {
     int rt, ct;
-    const int th = row_tile_rows(gm, p);
-    x.skinny = th != kTileI;
-    panel_order(ul, (gm + th - 1) / th, us.n_j, 4, &rt, &ct);
-    const int row0 = gs + rt * th;
-    x.i_valid = min(th, gm - rt * th);
+    panel_order(ul, (gm + kTileI - 1) / kTileI, us.n_j, 4, &rt, &ct);
+    const int row0 = gs + rt * kTileI;
+    x.i_valid = min(kTileI, gm - rt * kTileI);
     const int j0 = ct * kTileJ;
     x.nkr = ((OP == kFwd ? K : N) + kTileR - 1) / kTileR;
     x.nk = (x.nkr + 3) & ~3;
@@ -1273,215 +1262,6 @@ struct Pipe {
   }
 };
 
-// ---------------------------------------------------------------------------
-// skinny units (fwd/dgrad, groups of few rows)
-// ---------------------------------------------------------------------------
-// A group of at most skinny_rows rows would fill a 256-row tile with a few
-// real rows: its units would run 256-row MFMA work for every stage of its
-// weight panel and, with the stage ring shared by both operands, keep only
-// three 16 KiB weight stages in flight per CU.  Such a group is cut into units
-// of kSkinnyTileRows (32) rows x 256 columns instead, which stream their weight
-// panel at the memory system's pace:
-//  * each wave owns 64 of the 256 output columns and runs independently of the
-//    others (no barrier inside a unit);
-//  * operand B (the weights) goes through a wave-private ring of 8 LDS slots,
-//    4 KiB of each of the 8 stage arrays, filled by LDS-DMA: 7 stages (28 KiB
-//    per wave, 112 KiB per CU) are in flight while the current one is used;
-//  * operand A (X rows for fwd, G rows for dgrad; 32 rows) is loaded straight
-//    into registers in the MFMA layout, with the same 7-stage lead;
-//  * per 32-deep stage a wave runs 2 x 4 MFMAs of 16 x 16 x 32.
-// Every output element sums the same products in the same order through the
-// same instruction as in a 256-row tile, so a skinny unit's results are bit for
-// bit those of the same rows in a whole tile.
-constexpr int kSkSlots = 8;               // ring slots (stage arrays)
-constexpr int kSkAhead = kSkSlots - 1;    // stages in flight
-constexpr int kSkOps = 6;                 // vector memory operations per stage and wave: 4 B, 2 A
-constexpr int kSkWaveBytes = 4096;        // a wave's part of one slot
-static_assert(kSkinnyTileRows == 32, "the skinny pipeline holds two 16-row blocks");
-static_assert(kSkAhead * kSkOps < 64, "vmcnt range");
-
-template <int S>
-__device__ __forceinline__ uint8_t* sk_slot() {
-  if constexpr (S < 4) return stage_a<S>();
-  else return stage_b<S - 4>();
-}
-
-// dgrad's skinny B slice is 32 reduction rows x 64 columns (128-byte LDS rows);
-// 16-byte chunk c of row r lives at chunk c ^ swz_sk(r).  A transposing
-// fragment read touches rows 8g + t (or 8g + 4 + t), g, t = 0..3, 32 bytes
-// each; the swizzle gives the 8 even (and the 8 odd) rows of one read four
-// distinct chunk pairs, each twice, the minimum for 512 bytes per instruction.
-__device__ __forceinline__ int swz_sk(int r) { return 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)); }
-
-typedef f32x4 SkAcc[2][4];
-
-template <int OP, bool MASK>
-struct Skinny {
-  static constexpr bool BTC = (OP == kDgrad);  // W read along its columns
-  uint32_t off_b[4];  // this wave's 4 B loads of a stage (bytes from the stage's first element)
-  uint32_t cb_b[4];   // MASK (fwd): byte position of each B load within its 64-byte stage row
-  uint32_t off_a[2];  // A loads of row blocks 0, 1
-  uint32_t cb_a;      // byte position of this lane's A chunk within the 64-byte stage row
-  int w, lane;
-
-  __device__ __forceinline__ void init(const GemmParams& p, int w_, int lane_) {
-    w = w_;
-    lane = lane_;
-    const int ld_a = (OP == kFwd ? p.k : p.n) * 2;
-    const int ld_b = p.k * 2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (!BTC) {  // W rows 64 w + 16 q + l / 4, 64 bytes each
-        const int r = 16 * q + (lane >> 2);
-        const int c = (lane & 3) ^ swz_rc(r);
-        off_b[q] = (uint32_t)((64 * w + r) * ld_b + c * 16);
-        cb_b[q] = (uint32_t)(c * 16);
-      } else {     // reduction rows 8 q + l / 8, this wave's 128 bytes of each
-        const int r = 8 * q + (lane >> 3);
-        const int c = (lane & 7) ^ swz_sk(r);
-        off_b[q] = (uint32_t)(r * ld_b + 128 * w + c * 16);
-        cb_b[q] = 0;
-      }
-    }
-    cb_a = (uint32_t)((lane >> 4) * 16);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) off_a[rb] = (uint32_t)((16 * rb + (lane & 15)) * ld_a) + cb_a;
-  }
-
-  // The loads of stage kt: operand B into ring slot S (this wave's part), and
-  // operand A into registers.  Past the unit's last stage the buffers have no
-  // valid bytes: the loads return zeros and move no data.
-  template <int S>
-  __device__ __forceinline__ void issue(const Unit& x, int kt, bf16x8 (&fa)[2]) const {
-    const bool live = kt < x.nk;
-    uint8_t* lds = sk_slot<S>() + w * kSkWaveBytes;
-    const DmaStage db = dma_begin<BTC>(x.b, lds, kt, live);
-    const uint32_t kvb = MASK && !BTC ? stage_valid_bytes(x.b, kt) : 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t off = (MASK && !BTC && cb_b[q] >= kvb) ? kOutOfRange : off_b[q];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(db.rs, (lds_void*)(lds + q * 1024), 16, off, 0, 0, 0);
-    }
-    const DmaStage da = dma_begin<false>(x.a, lds, kt, live);
-    const uint32_t kva = MASK ? stage_valid_bytes(x.a, kt) : 0;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const uint32_t off = (MASK && cb_a >= kva) ? kOutOfRange : off_a[rb];
-      fa[rb] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(da.rs, off, 0, 0));
-    }
-  }
-
-  // B fragment jb (16 of this wave's 64 columns, all 32 reductions) of slot S.
-  template <int S>
-  __device__ __forceinline__ bf16x8 frag_b(int jb) const {
-    const uint8_t* st = sk_slot<S>() + w * kSkWaveBytes;
-    if constexpr (!BTC) {
-      return load_frag<false>(st, 16 * jb, lane);
-    } else {
-      // as load_frag<true>, on 128-byte rows: lane s of group g reads row
-      // 8 g + s / 4 (and 4 rows further), columns 16 jb + 4 (s % 4) .. + 3
-      const int g = lane >> 4, sl = lane & 15;
-      const int r = 8 * g + (sl >> 2);
-      const int chunk = (2 * jb + ((sl >> 1) & 1)) ^ swz_sk(r);  // swz_sk(r + 4) == swz_sk(r)
-      const uint8_t* p0 = st + r * 128 + chunk * 16 + (sl & 1) * 8;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0));
-      const s16x4 hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p0 + 4 * 128));
-      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-  }
-
-  // Stage kt (slot S): issue stage kt + 7 into the slot stage kt - 1 used (its
-  // fragments were read and its MFMAs issued in the previous step), wait until
-  // stage kt has landed (the 7 stages issued after it may still be in flight),
-  // read its B fragments and run its 8 MFMAs.
-  template <int S>
-  __device__ __forceinline__ void step(SkAcc& acc, bf16x8 (&fa)[kSkSlots][2], const Unit& x, int kt) const {
-    constexpr int SN = (S + kSkAhead) % kSkSlots;
-    // The order issue -> wait -> reads is what makes the wait count right (the
-    // compiler does not track the LDS-DMA into the slot): pin it.
-    __builtin_amdgcn_sched_barrier(0);
-    issue<SN>(x, kt + kSkAhead, fa[SN]);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm_lgkm<kSkAhead * kSkOps>();
-    __builtin_amdgcn_sched_barrier(0);
-    bf16x8 fb[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) fb[jb] = frag_b<S>(jb);
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-      for (int ib = 0; ib < 2; ++ib) mfma_block(acc[ib][jb], fb[jb], fa[S][ib]);
-  }
-
-  // The whole unit: prologue, stages, store.  Leaves no memory operation of
-  // its loads outstanding; returns the stores it issued.
-  __device__ __forceinline__ int run(const Unit& x) const {
-    SkAcc acc;
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[ib][jb][e] = 0.0f;
-    bf16x8 fa[kSkSlots][2];
-    issue<0>(x, 0, fa[0]);
-    issue<1>(x, 1, fa[1]);
-    issue<2>(x, 2, fa[2]);
-    issue<3>(x, 3, fa[3]);
-    issue<4>(x, 4, fa[4]);
-    issue<5>(x, 5, fa[5]);
-    issue<6>(x, 6, fa[6]);
-    // nk is a multiple of 4; the steps past it multiply the zeros their dead
-    // loads returned (acc + 0 == acc: an accumulator started at +0.0 is never -0.0)
-    for (int kt = 0; kt < x.nk; kt += kSkSlots) {
-      step<0>(acc, fa, x, kt);
-      step<1>(acc, fa, x, kt + 1);
-      step<2>(acc, fa, x, kt + 2);
-      step<3>(acc, fa, x, kt + 3);
-      step<4>(acc, fa, x, kt + 4);
-      step<5>(acc, fa, x, kt + 5);
-      step<6>(acc, fa, x, kt + 6);
-      step<7>(acc, fa, x, kt + 7);
-    }
-    wait_vm_lgkm<0>();  // the dead loads of the last steps have landed (they wrote LDS)
-    return x.mode == kStoreBf16 ? store<kStoreBf16>(acc, x) : store<kStoreF32>(acc, x);
-  }
-
-  // Stores this wave's 32 x 64 block from the MFMA layout (lane l holds row
-  // 16 ib + l % 16, columns 16 jb + 4 (l / 16) .. + 3 of block ib, jb); a skinny
-  // unit writes 16 KiB (bf16), so the stores are not staged.  Rows past i_valid
-  // and columns past j_valid (a multiple of 8) are outside the descriptor's
-  // range or get an out-of-range offset.
-  template <int mode>
-  __device__ __forceinline__ int store(const SkAcc& acc, const Unit& x) const {
-    constexpr int esz = mode == kStoreBf16 ? 2 : 4;
-    const int ldc_b = (int)x.ldc * esz;
-    const int extent = x.i_valid > 0 ? (x.i_valid - 1) * ldc_b + x.j_valid * esz : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(x.out, 0, extent, 0x00020000);
-    const int ln = lane_here();
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const int row = 16 * ib + (ln & 15);
-        const int col = 64 * w + 16 * jb + 4 * (ln >> 4);
-        const uint32_t off = col < x.j_valid ? (uint32_t)(row * ldc_b + col * esz) : kOutOfRange;
-        const f32x4& a = acc[ib][jb];
-        if constexpr (mode == kStoreBf16) {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(acc_read(a[0]), acc_read(a[1]));
-          pk[1] = pack_bf16x2(acc_read(a[2]), acc_read(a[3]));
-          __builtin_amdgcn_raw_buffer_store_b64(pk, rs, off, 0, 0);
-        } else {
-          const f32x4 v = {acc_read(a[0]), acc_read(a[1]), acc_read(a[2]), acc_read(a[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
-        }
-      }
-    return 8;
-  }
-};
-
 // The epilogue of one unit in its store mode; returns the number of vector
 // memory operations it issued.
 template <int OP, int OUT>
@@ -1574,33 +1354,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
 #pragma unroll 1
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_s_sleep(127);
   }
-  Skinny<OP, MASK> sk;
-  if constexpr (OP != kWgrad) sk.init(p, pipe.w, pipe.lane);
   Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
-  if (cur.valid && !cur.skinny) {
+  if (cur.valid) {
     pipe.prefetch_first(cur);
     pipe.issue_last(cur);
   }
   int tail = 0;  // memory operations issued between stage 2 and stage 3's operand A of the current unit
   for (int u = vb; cur.valid; u += P) {
-    if constexpr (OP != kWgrad) {
-      if (cur.skinny) {
-        // a self-contained unit: its loads have all landed when run() returns,
-        // so the stores it leaves in flight are older than anything the next
-        // unit waits for; the barrier keeps the next whole unit's loads out of
-        // the ring slots until every wave is done reading them
-        sk.run(cur);
-        lds_barrier();
-        const Unit nxt = decode_item<OP>(p, tb, us, total, pl, u + P);
-        if (nxt.valid && !nxt.skinny) {
-          pipe.prefetch_first(nxt);
-          pipe.issue_last(nxt);
-        }
-        tail = 0;
-        cur = nxt;
-        continue;
-      }
-    }
     Acc acc;
 #pragma unroll
     for (int ib = 0; ib < 8; ++ib)
@@ -1649,8 +1409,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     // (the last stage buffers, 8 KiB per wave) to memory; operand A of stage 3
     // follows once every wave is done with them.
     const Unit nxt = decode_item<OP>(p, tb, us, total, pl, u + P);
-    const bool pre = nxt.valid && !nxt.skinny;  // a skinny unit loads its own first stages
-    if (pre) pipe.prefetch_first(nxt);
+    if (nxt.valid) pipe.prefetch_first(nxt);
     const int ln = lane_here();
     const OutTile ot = out_tile(cur.out, cur.ldc, cur.i_valid, cur.j_valid, pipe.wi, pipe.wj, ln,
                                 is_bf16_mode(cur.mode) ? 2 : 4);
@@ -1662,7 +1421,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     else tail = run_epilogue<OP, OUT>(acc, cur, ot, s_b3 + (pipe.w & 1) * 8192, ln, rmw);
     wait_vm_lgkm<63>();  // the staging reads have returned ...
     lds_barrier();       // ... in every wave
-    if (pre) pipe.issue_last(nxt);
+    if (nxt.valid) pipe.issue_last(nxt);
     cur = nxt;
   }
   wait_vm_lgkm<0>();

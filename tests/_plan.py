@@ -1,23 +1,16 @@
-"""The fwd/dgrad work plan restated for tests: how many units a call has and
-which of them the tail split cuts (so tests can assert which cases exercise a
-split).  Mirrors the rule the C ABI header documents: a group of at most 64
-rows is cut into row tiles of 32 rows (skinny units), a larger one into row
-tiles of 256; each row tile times the 256-wide column tiles is one unit.  With
-U units, T = U mod 256 tail units are cut into S = min(256 // T, 8, groups of 4
+"""The fwd/dgrad work plan restated for tests: how many 256 x 256 units a call
+has and which of them the tail split cuts (so tests can assert which cases
+exercise a split).  Mirrors the rule the C ABI header documents: with U units,
+T = U mod 256 tail units are cut into S = min(256 // T, 8, groups of 4
 reduction stages, slots // T) pieces when S >= 2."""
 import math
 
 BALANCE, MAX_SPLIT = 256, 8
-SKINNY_MAX_ROWS, SKINNY_TILE = 64, 32
-
-
-def tile_rows(m):
-    return SKINNY_TILE if int(m) <= SKINNY_MAX_ROWS else 256
 
 
 def units(op, sizes, N, K):
     n_j = math.ceil(N / 256) if op == "fwd" else math.ceil(K / 256)
-    return sum(math.ceil(int(m) / tile_rows(m)) for m in sizes) * n_j
+    return sum(math.ceil(int(m) / 256) for m in sizes) * n_j
 
 
 def slots(op, M, N, K, E):
@@ -46,7 +39,7 @@ def unit_tiles(op, sizes, N, K):
     n_j = math.ceil(N / 256) if op == "fwd" else math.ceil(K / 256)
     out = []
     for e, m in enumerate(sizes):
-        rows = math.ceil(int(m) / tile_rows(m))
+        rows = math.ceil(int(m) / 256)
         for ul in range(rows * n_j):
             per_panel = 4 * n_j
             panel = ul // per_panel
@@ -67,8 +60,7 @@ def split_mask(op, sizes, N, K, M=None, E=None):
     mask = np.zeros((int(starts[-1]), n_j), dtype=bool)
     if T:
         for e, rt, ct in unit_tiles(op, sizes, N, K)[U - T:]:
-            th = tile_rows(sizes[e])
-            r0 = int(starts[e]) + th * rt
-            r1 = min(int(starts[e + 1]), r0 + th)
+            r0 = int(starts[e]) + 256 * rt
+            r1 = min(int(starts[e + 1]), r0 + 256)
             mask[r0:r1, ct] = True
     return mask, (U, T, S)
