@@ -48,7 +48,8 @@ def parse():
     from workloads import CONFIGS
     ap.add_argument("--workload", default="mixtral", choices=list(CONFIGS))
     ap.add_argument("--reps", type=int, default=10,
-                    help="timed reps per operation in the per-operation protocol")
+                    help="timed reps per operation in the per-operation protocol (0: skip it, and the "
+                         "host-call latency, e.g. under a profiler)")
     ap.add_argument("--configs", default=",".join(OTHER_CONFIGS),
                     help="comma-separated workloads measured per operation besides --workload "
                          "('none' for none)")
@@ -473,8 +474,8 @@ def main():
     # per-operation protocol on this workload, then host-call latency
     flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
     print("bench: per-operation protocol", file=sys.stderr, flush=True)
-    protocol = ops_report(measure_ops(torch, run, mg, mg0, args.reps, 3, flush), d)
-    host_us = host_call_latency(torch, mdg, run)
+    protocol = ops_report(measure_ops(torch, run, mg, mg0, args.reps, 3, flush), d) if args.reps > 0 else None
+    host_us = host_call_latency(torch, mdg, run) if args.reps > 0 else None
 
     autograd = None
     if not args.no_autograd:
@@ -490,7 +491,7 @@ def main():
     del run, d, x, w, g, offs, mg, mg0, y, dx
     torch.cuda.empty_cache()
     configs = {}
-    names = [] if args.configs in ("", "none") else [c for c in args.configs.split(",") if c != args.workload]
+    names = [] if args.configs in ("", "none") or args.reps <= 0 else [c for c in args.configs.split(",") if c != args.workload]
     for name in names:
         print(f"bench: per-operation protocol on {name}", file=sys.stderr, flush=True)
         dc = make_inputs(name, seed=0, device=dev, tensors=("x", "w", "g", "main_grad"))
