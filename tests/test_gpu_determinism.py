@@ -65,6 +65,27 @@ def test_accumulate_equals_adding_own_dw():
     assert not torch.signbit(outs[0][0, :3, :5]).any()      # -0.0 + 0.0 = +0.0
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_accumulate_all_groups_empty_with_padding_rows(dtype):
+    """m_rows > 0 but every group empty (offs all 0, the rows are padding): the
+    accumulate adds the zero dW like adding the library's own overwrite dW does,
+    so -0.0 becomes +0.0 and every other value is unchanged.  (m_rows == 0, the
+    pages' sum_m == 0, launches nothing: see the next test.)"""
+    E, N, K, M = 3, 256, 64, 37
+    d = make_inputs(sizes=[0, 0, 0], N=N, K=K, extra_rows=M, seed=8, device=DEV, tensors=("x", "g"))
+    mg0 = torch.randn((E, N, K), device=DEV).to(dtype)
+    mg0[0, 0, :7] = -0.0
+    dw = mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out_dtype=dtype)
+    expect = mg0.clone().add_(dw)
+    mg = mg0.clone()
+    mdg.grouped_det_gemm_wgrad(d["g"], d["x"], d["offs"], out=mg, accumulate=True)
+    torch.cuda.synchronize()
+    iv = torch.int32 if dtype == torch.float32 else torch.int16
+    assert torch.all(dw.view(iv) == 0)
+    assert torch.equal(mg.view(iv), expect.view(iv))
+    assert not torch.signbit(mg[0, 0, :7].float()).any()
+
+
 def test_accumulate_zero_rows_leaves_out_unchanged():
     E, N, K = 3, 256, 64
     g = torch.empty((0, N), dtype=torch.bfloat16, device=DEV)
