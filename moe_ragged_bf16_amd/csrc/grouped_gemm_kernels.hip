@@ -26,7 +26,8 @@
 //    by buffer loads that write LDS directly (no registers); the buffer range
 //    check turns rows past a group's or chunk's end into zeros.  Up to three
 //    stages are in flight while the MFMAs of the current one run; the next
-//    unit's first stages load during the current epilogue.  Where an operand is
+//    unit's first stages load during the current epilogue.  A wgrad unit of at
+//    most 96 rows runs its few stages from those alone.  Where an operand is
 //    read along its rows (fwd; dgrad's A), two consecutive stages hold the two
 //    halves of each 128-byte line and are loaded as a pair, so that the L1
 //    fetches every line from the L2 once (see Pipe::kPairs).
@@ -480,6 +481,15 @@ constexpr int frag_reads() { return TC ? 2 : 1; }
 // (Each accumulator's next MFMA is 32 MFMAs later, and the epilogue reads them
 // after a barrier.)
 typedef f32x4 Acc[8][8];
+
+__device__ __forceinline__ void zero(Acc& acc) {
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) acc[ib][jb][x] = 0.0f;
+}
 
 __device__ __forceinline__ void mfma_block(f32x4& c, const bf16x8& b, const bf16x8& a) {
   asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(b), "v"(a));
@@ -1036,6 +1046,29 @@ struct Pipe {
     }
   }
 
+  // A short unit: a wgrad unit of fewer than 4 real stages (a group or row
+  // chunk of at most 96 rows; most units of workloads with many small
+  // experts).  Its real stages are all loaded ahead, nothing more (the stages
+  // past them would hold zeros, whose products leave every accumulator bit as
+  // it is), and it runs them without the ring.  fwd and dgrad reduce over K or
+  // N and have no short units.
+  static __device__ __forceinline__ bool is_short(const Unit& x) { return OP == kWgrad && x.nkr < 4; }
+
+  // Stage S of a short unit (landed in every wave): the same MFMAs, in the
+  // same order per accumulator, as a step of the ring.
+  template <int S>
+  __device__ __forceinline__ void short_stage(Acc& acc) const {
+    bf16x8 fa[2][4], fb[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) fb[b] = load_frag<BTC>(stage_b<S>(), wj * 128 + 16 * b, lane);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) fa[b >> 2][b & 3] = load_frag<ATC>(stage_a<S>(), wi * 128 + 16 * b, lane);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) mma_col(acc, fb[jb], fa[0], 0, jb);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) mma_col(acc, fb[jb], fa[1], 4, jb);
+  }
+
   // A unit's first stages, loaded while the previous unit's epilogue runs (or
   // at the start): stages 0..2, and operand A of stage 3 (kPairs: stages 0 and
   // 1 as a pair, then stage 2).  The rest of stage 3 follows the epilogue
@@ -1294,14 +1327,17 @@ __device__ __forceinline__ int run_epilogue(const Acc& acc, const Unit& cur, con
 }
 
 // Per unit, with stages of 32 reductions in a ring of 4 LDS buffers:
-//   * stages 0..2 and operand A of stage 3 are loaded ahead (for every unit
-//     but the first, during the previous unit's epilogue);
+//   * stages 0..2 are loaded ahead (for every unit but the first, during the
+//     previous unit's epilogue), operand A of stage 3 right after it;
 //   * stage kt: issue operand B of stage kt+3 into the buffer stage kt-1 used;
 //     read the second half of stage kt's fragments while the MFMAs of its
 //     first half run; wait for stage kt+1 and pass one barrier; issue operand
 //     A of stage kt+4 into stage kt's buffer and read the first half of stage
 //     kt+1's fragments while the MFMAs of stage kt's second half run.
-// One barrier per stage, and no MFMA waits on an LDS read.
+// One barrier per stage, and no MFMA waits on an LDS read.  A wgrad unit of at
+// most 3 real stages (a short unit) has them all loaded ahead and runs them
+// without the ring, so no load follows the previous epilogue's stores and its
+// own end does not wait for them (vector memory operations complete in order).
 // OUT: the output's store mode (bf16 for fwd and dgrad; bf16, fp32 or their
 // accumulating forms for wgrad).  Units of split wgrad experts store fp32
 // partials.
@@ -1355,59 +1391,73 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     for (int i = 0; i < 2; ++i) __builtin_amdgcn_s_sleep(127);
   }
   Unit cur = decode_item<OP>(p, tb, us, total, pl, vb);
-  if (cur.valid) {
-    pipe.prefetch_first(cur);
-    pipe.issue_last(cur);
-  }
+  if (cur.valid) pipe.prefetch_first(cur);
   int tail = 0;  // memory operations issued between stage 2 and stage 3's operand A of the current unit
   for (int u = vb; cur.valid; u += P) {
     Acc acc;
-#pragma unroll
-    for (int ib = 0; ib < 8; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-        for (int x = 0; x < 4; ++x) acc[ib][jb][x] = 0.0f;
-
     const bool rmw = (OUT == kStoreF32Acc || OUT == kStoreBf16Acc) && cur.mode == OUT;
-    if (cur.nk > 0) {
-      bf16x8 fbA[8], fbB[8], fal[4], fah[4];
-      int e1 = tail, e2 = 0;
-      wait_vm(Pp::kAfterStage0 + tail);  // stage 0 (kPairs: stages 0, 1) has landed
-      lds_barrier();                     // ... in every wave
-      pipe.first_frags(fbA, fal);
-      // nk is a positive multiple of 4: the first 4 steps, then the steady state
-      // The first 4 steps always run; after them, steps of stages past nkr
-      // (zeros) are skipped.  A step's wait counts only loads issued before it
-      // (by the prefetch and earlier steps), so leaving out the last steps
-      // changes no wait; their loads, already in flight, drain at the wait
-      // after the loop.  (Guarding the first 4 steps as well made the compiler
-      // schedule the whole loop worse: measured 3-5 % slower.)
-      const int nkr = cur.nkr;
-      pipe.template step<0, true>(acc, fbA, fbB, fal, fah, cur, 0, e1, e2);
-      pipe.template step<1, true>(acc, fbB, fbA, fal, fah, cur, 1, e1, e2);
-      pipe.template step<2, true>(acc, fbA, fbB, fal, fah, cur, 2, e1, e2);
-      pipe.template step<3, true>(acc, fbB, fbA, fal, fah, cur, 3, e1, e2);
-      int kt = 4;
-      for (; kt + 4 <= nkr; kt += 4) {
-        pipe.template step<0, false>(acc, fbA, fbB, fal, fah, cur, kt, e1, e2);
-        pipe.template step<1, false>(acc, fbB, fbA, fal, fah, cur, kt + 1, e1, e2);
-        pipe.template step<2, false>(acc, fbA, fbB, fal, fah, cur, kt + 2, e1, e2);
-        pipe.template step<3, false>(acc, fbB, fbA, fal, fah, cur, kt + 3, e1, e2);
+    if (Pp::is_short(cur)) {
+      zero(acc);
+      // All of this unit's stages were loaded ahead; only the previous unit's
+      // epilogue operations were issued after them, and those stores drain
+      // while this unit computes and stages its own results (no load of this
+      // unit is in flight at its end, so nothing waits for them here).
+      if (cur.nkr > 0) {
+        wait_vm(tail);  // this unit's stages have landed ...
+        lds_barrier();  // ... in every wave
+        pipe.template short_stage<0>(acc);
+        if (cur.nkr > 1) pipe.template short_stage<1>(acc);
+        if (cur.nkr > 2) pipe.template short_stage<2>(acc);
       }
-      if (kt < nkr) {
-        pipe.template step<0, false>(acc, fbA, fbB, fal, fah, cur, kt, e1, e2);
-        if (kt + 1 < nkr) pipe.template step<1, false>(acc, fbB, fbA, fal, fah, cur, kt + 1, e1, e2);
-        if (kt + 2 < nkr) pipe.template step<2, false>(acc, fbA, fbB, fal, fah, cur, kt + 2, e1, e2);
+      wait_vm_lgkm<63>();  // this wave's LDS reads have returned ...
+      lds_barrier();       // ... in every wave, before the next unit's loads
+    } else {
+      // The rest of stage 3, now that the previous epilogue is done with its
+      // buffers.  Issued only here, by a unit that drains all its loads before
+      // its epilogue, so no stage load is ever in flight into the staging
+      // buffers when an epilogue (of either kind of unit) writes them, and the
+      // compiler sees as much.
+      pipe.issue_last(cur);
+      zero(acc);
+      if (cur.nk > 0) {
+        bf16x8 fbA[8], fbB[8], fal[4], fah[4];
+        int e1 = tail, e2 = 0;
+        wait_vm(Pp::kAfterStage0 + tail);  // stage 0 (kPairs: stages 0, 1) has landed
+        lds_barrier();                     // ... in every wave
+        pipe.first_frags(fbA, fal);
+        // nk is a positive multiple of 4: the first 4 steps, then the steady state
+        // The first 4 steps always run; after them, steps of stages past nkr
+        // (zeros) are skipped.  A step's wait counts only loads issued before it
+        // (by the prefetch and earlier steps), so leaving out the last steps
+        // changes no wait; their loads, already in flight, drain at the wait
+        // after the loop.  (Guarding the first 4 steps as well made the compiler
+        // schedule the whole loop worse: measured 3-5 % slower.)
+        const int nkr = cur.nkr;
+        pipe.template step<0, true>(acc, fbA, fbB, fal, fah, cur, 0, e1, e2);
+        pipe.template step<1, true>(acc, fbB, fbA, fal, fah, cur, 1, e1, e2);
+        pipe.template step<2, true>(acc, fbA, fbB, fal, fah, cur, 2, e1, e2);
+        pipe.template step<3, true>(acc, fbB, fbA, fal, fah, cur, 3, e1, e2);
+        int kt = 4;
+        for (; kt + 4 <= nkr; kt += 4) {
+          pipe.template step<0, false>(acc, fbA, fbB, fal, fah, cur, kt, e1, e2);
+          pipe.template step<1, false>(acc, fbB, fbA, fal, fah, cur, kt + 1, e1, e2);
+          pipe.template step<2, false>(acc, fbA, fbB, fal, fah, cur, kt + 2, e1, e2);
+          pipe.template step<3, false>(acc, fbB, fbA, fal, fah, cur, kt + 3, e1, e2);
+        }
+        if (kt < nkr) {
+          pipe.template step<0, false>(acc, fbA, fbB, fal, fah, cur, kt, e1, e2);
+          if (kt + 1 < nkr) pipe.template step<1, false>(acc, fbB, fbA, fal, fah, cur, kt + 1, e1, e2);
+          if (kt + 2 < nkr) pipe.template step<2, false>(acc, fbA, fbB, fal, fah, cur, kt + 2, e1, e2);
+        }
       }
+      wait_vm_lgkm<0>();
+      __syncthreads();  // every wave is done reading LDS before the next unit's loads
     }
-    wait_vm_lgkm<0>();
-    __syncthreads();  // every wave is done reading LDS before the next unit's loads
 
     // Epilogue, overlapped with the next unit's first stages: stages 0..2 load
     // into their buffers while the results pass through the staging buffers
     // (the last stage buffers, 8 KiB per wave) to memory; operand A of stage 3
-    // follows once every wave is done with them.
+    // follows once every wave is done with them (at the top of the next unit).
     const Unit nxt = decode_item<OP>(p, tb, us, total, pl, u + P);
     if (nxt.valid) pipe.prefetch_first(nxt);
     const int ln = lane_here();
@@ -1421,7 +1471,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GemmParams p)
     else tail = run_epilogue<OP, OUT>(acc, cur, ot, s_b3 + (pipe.w & 1) * 8192, ln, rmw);
     wait_vm_lgkm<63>();  // the staging reads have returned ...
     lds_barrier();       // ... in every wave
-    if (nxt.valid) pipe.issue_last(nxt);
     cur = nxt;
   }
   wait_vm_lgkm<0>();
