@@ -13,7 +13,8 @@ step's dominant kernel against the MI355X dense bf16 MFMA peak (or HBM below
 the ridge point).  `ops` and `configs` follow the per-operation protocol: each
 operation alone, a 1 GiB buffer written before every rep to flush the L2s and
 the MALL, the median of the HIP-event times; `configs` covers the other
-workloads (tiny, fine-grained, skewed, accumulate stress) that way.
+workloads (tiny, fine-grained, skewed, accumulate stress, and the gate_up and
+down projection shapes at 4, 8, 16 and 32 experts) that way.
 `cpu_baseline` times the fp32 CPU oracle on a bounded sample of the workload.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload mixtral]
@@ -36,7 +37,9 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E (published)
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # FLOP per byte
 OPS = ("fwd", "dgrad", "wgrad_bf16", "wgrad_fp32", "wgrad_fp32_accumulate")
-OTHER_CONFIGS = ("tiny", "fine", "skewed", "stress")
+OTHER_CONFIGS = ("tiny", "fine", "skewed", "stress",
+                 "gate_up_e4", "down_e4", "gate_up_e8", "down_e8",
+                 "gate_up_e16", "down_e16", "gate_up_e32", "down_e32")
 FLUSH_BYTES = 1 << 30
 
 
