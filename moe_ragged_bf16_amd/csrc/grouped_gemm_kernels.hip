@@ -1048,10 +1048,11 @@ struct Pipe {
 
   // A short unit: a wgrad unit of fewer than 4 real stages (a group or row
   // chunk of at most 96 rows; most units of workloads with many small
-  // experts).  Its real stages are all loaded ahead, nothing more (the stages
-  // past them would hold zeros, whose products leave every accumulator bit as
-  // it is), and it runs them without the ring.  fwd and dgrad reduce over K or
-  // N and have no short units.
+  // experts).  Stages 0..2 are loaded ahead as for every unit (those past its
+  // last real stage load zeros and move no memory), it issues no other load,
+  // and it runs its real stages without the ring: the stages it leaves out
+  // would only add products of zeros, which leave every accumulator bit as it
+  // is.  fwd and dgrad reduce over K or N and have no short units.
   static __device__ __forceinline__ bool is_short(const Unit& x) { return OP == kWgrad && x.nkr < 4; }
 
   // Stage S of a short unit (landed in every wave): the same MFMAs, in the
@@ -1070,9 +1071,10 @@ struct Pipe {
   }
 
   // A unit's first stages, loaded while the previous unit's epilogue runs (or
-  // at the start): stages 0..2, and operand A of stage 3 (kPairs: stages 0 and
-  // 1 as a pair, then stage 2).  The rest of stage 3 follows the epilogue
-  // (issue_last), whose staging buffers are stage 3's.
+  // at the start): stages 0..2 (kPairs: stages 0 and 1 as a pair, then stage
+  // 2).  Stage 3 (its operand A; fwd: all of it) follows once the epilogue,
+  // which stages its results through stage 3's buffers, is done (issue_last,
+  // at the top of a ring unit).
   __device__ __forceinline__ void prefetch_first(const Unit& x) const {
     if constexpr (kPairB) {
       issue_a_pair<0>(x, 0);
